@@ -1,0 +1,36 @@
+"""CPU oracle for the weight-informed activation-sparse linear (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this package:
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may call it. It shares no code with the HIP library; both sides
+take their inputs from ``workloads``.
+
+Every function restates, in plain slow code, what the pages define:
+
+* WINA article (arXiv:2505.19427, lsdiaocha.cn), section 一 (weight-aware
+  activation): the gate keeps input j when |x_j * c_j| is among the K largest
+  entries of |x (.) c|, c being the column-wise L2 norm of W.
+* Spark Transformer article, section 2.2 (statistical top-k operator): fit a
+  Gaussian to the vector (mean, population variance) and keep the entries
+  above mu + sigma * Phi^-1(1 - s).
+* Spark Transformer article, section 3.1 (sparse matrix multiplication, the
+  index-list product): y accumulates x_j times the weight vector of input j
+  over the active indices only.
+
+Parity status of each function is listed in ``oracle.sparse_linear``.
+"""
+from .sparse_linear import (  # noqa: F401
+    as_f64,
+    column_norms,
+    scores,
+    topk_gate,
+    stat_moments,
+    stat_threshold,
+    stat_gate,
+    normal_quantile,
+    active_indices,
+    sparse_product,
+    sparse_product_rows,
+    gate,
+    forward,
+)
