@@ -1,0 +1,235 @@
+"""Python binding of the weight-informed activation-sparse linear (C ABI in
+include/sparse_linear.h, HIP kernels for gfx950 in csrc/).
+
+Argument marshalling only: every step of the forward runs in the library's
+kernels. PyTorch supplies device memory and streams. Loading fails loudly when
+the built library is missing; there is no fallback path.
+
+The functions below carry the C names; ``SparseLinear`` wraps a handle for
+torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_linear.so")
+
+SL_OK, SL_ERR_ARG, SL_ERR_UNSUPPORTED, SL_ERR_OOM, SL_ERR_HIP = 0, 1, 2, 3, 4
+SL_F32, SL_BF16 = 0, 1
+SL_W_ROWMAJOR_OUT_IN, SL_W_COLMAJOR = 0, 1
+SL_GATE_TOPK, SL_GATE_STAT, SL_GATE_FIXED = 0, 1, 2
+SL_MAX_N, SL_MAX_BATCH = 32768, 16
+
+EXPORTED = [
+    "sparse_linear_init", "sparse_linear_forward", "sparse_linear_forward_dense",
+    "sparse_linear_get_norms", "sparse_linear_destroy", "sparse_linear_strerror",
+    "sparse_linear_last_error", "sparse_linear_normal_quantile",
+    "sparse_linear_timing_enable", "sparse_linear_timing_read", "sparse_linear_set_plan",
+]
+
+_lib: Optional[ctypes.CDLL] = None
+
+_vp, _i64, _i32, _dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
+
+
+class SparseLinearError(RuntimeError):
+    def __init__(self, status: int, where: str, msg: str):
+        super().__init__(f"{where}: status {status}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded shared library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m free_activation_sparse_amd.build)")
+    L = ctypes.CDLL(LIB_PATH)
+    L.sparse_linear_init.argtypes = [ctypes.POINTER(_vp), _vp, ctypes.c_int, ctypes.c_int, _i64, _i64, _vp,
+                                     ctypes.c_int, _i64, _dbl, _i32, _vp]
+    L.sparse_linear_init.restype = ctypes.c_int
+    L.sparse_linear_forward.argtypes = [_vp, _vp, _i32, _vp, ctypes.c_int, _vp, _vp, _vp, _vp]
+    L.sparse_linear_forward.restype = ctypes.c_int
+    L.sparse_linear_forward_dense.argtypes = [_vp, _vp, _i32, _vp, ctypes.c_int, _vp]
+    L.sparse_linear_forward_dense.restype = ctypes.c_int
+    L.sparse_linear_get_norms.argtypes = [_vp, _vp, _vp]
+    L.sparse_linear_get_norms.restype = ctypes.c_int
+    L.sparse_linear_destroy.argtypes = [_vp]
+    L.sparse_linear_destroy.restype = ctypes.c_int
+    L.sparse_linear_strerror.argtypes = [ctypes.c_int]
+    L.sparse_linear_strerror.restype = ctypes.c_char_p
+    L.sparse_linear_last_error.argtypes = []
+    L.sparse_linear_last_error.restype = ctypes.c_char_p
+    L.sparse_linear_normal_quantile.argtypes = [_dbl]
+    L.sparse_linear_normal_quantile.restype = _dbl
+    L.sparse_linear_timing_enable.argtypes = [_vp, _i32]
+    L.sparse_linear_timing_enable.restype = ctypes.c_int
+    L.sparse_linear_timing_read.argtypes = [_vp, ctypes.POINTER(_dbl), ctypes.POINTER(_dbl), ctypes.POINTER(_i64)]
+    L.sparse_linear_timing_read.restype = ctypes.c_int
+    L.sparse_linear_set_plan.argtypes = [_vp, _i32, _i32]
+    L.sparse_linear_set_plan.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != SL_OK:
+        msg = lib().sparse_linear_last_error().decode(errors="replace")
+        raise SparseLinearError(status, where, msg or lib().sparse_linear_strerror(status).decode())
+
+
+# ------------------------------------------------------------------ C names
+def sparse_linear_init(W_ptr: int, w_dtype: int, w_layout: int, m: int, n: int, c_ptr: int, gate: int,
+                       K: int, s_keep: float, max_batch: int, stream: int) -> int:
+    h = _vp()
+    _check(lib().sparse_linear_init(ctypes.byref(h), W_ptr, w_dtype, w_layout, m, n, c_ptr or None, gate,
+                                    K, s_keep, max_batch, stream or None), "sparse_linear_init")
+    return h.value
+
+
+def sparse_linear_forward(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, mask_ptr: int = 0,
+                          count_ptr: int = 0, thresh_ptr: int = 0, stream: int = 0) -> None:
+    _check(lib().sparse_linear_forward(h, x_ptr, B, y_ptr, y_dtype, mask_ptr or None, count_ptr or None,
+                                       thresh_ptr or None, stream or None), "sparse_linear_forward")
+
+
+def sparse_linear_forward_dense(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, stream: int = 0) -> None:
+    _check(lib().sparse_linear_forward_dense(h, x_ptr, B, y_ptr, y_dtype, stream or None),
+           "sparse_linear_forward_dense")
+
+
+def sparse_linear_get_norms(h: int, c_ptr: int, stream: int = 0) -> None:
+    _check(lib().sparse_linear_get_norms(h, c_ptr, stream or None), "sparse_linear_get_norms")
+
+
+def sparse_linear_destroy(h: int) -> None:
+    _check(lib().sparse_linear_destroy(h), "sparse_linear_destroy")
+
+
+def sparse_linear_strerror(status: int) -> str:
+    return lib().sparse_linear_strerror(status).decode()
+
+
+def sparse_linear_last_error() -> str:
+    return lib().sparse_linear_last_error().decode(errors="replace")
+
+
+def sparse_linear_normal_quantile(p: float) -> float:
+    return lib().sparse_linear_normal_quantile(p)
+
+
+def sparse_linear_timing_enable(h: int, on: bool) -> None:
+    _check(lib().sparse_linear_timing_enable(h, 1 if on else 0), "sparse_linear_timing_enable")
+
+
+def sparse_linear_timing_read(h: int):
+    g, p, f = _dbl(), _dbl(), _i64()
+    _check(lib().sparse_linear_timing_read(h, ctypes.byref(g), ctypes.byref(p), ctypes.byref(f)),
+           "sparse_linear_timing_read")
+    return g.value, p.value, f.value
+
+
+def sparse_linear_set_plan(h: int, rows_per_tile: int, splits: int) -> None:
+    _check(lib().sparse_linear_set_plan(h, rows_per_tile, splits), "sparse_linear_set_plan")
+
+
+# ------------------------------------------------------------------ torch wrapper
+class SparseLinear:
+    """One linear layer behind a library handle.
+
+    ``W`` is a CUDA tensor [m][n] (nn.Linear layout) or, with
+    ``layout='colmajor'``, the column-major [n][m] tensor; bf16 or fp32.
+    ``gate`` is 'topk' (with K), 'stat' (with s_keep) or 'fixed' (with tau).
+    """
+
+    def __init__(self, W, c=None, gate: str = "topk", K: int = 0, s_keep: float = 0.0,
+                 tau: float = 0.0, max_batch: int = 1, layout: str = "rowmajor", m: int = None,
+                 n: int = None):
+        import torch
+        if not W.is_cuda:
+            raise ValueError("W must be a device tensor")
+        self._torch = torch
+        self.dtype = W.dtype
+        self.w_dtype = {torch.bfloat16: SL_BF16, torch.float32: SL_F32}[W.dtype]
+        if layout == "rowmajor":
+            m, n = W.shape
+            lay = SL_W_ROWMAJOR_OUT_IN
+        else:
+            n, m = W.shape
+            lay = SL_W_COLMAJOR
+        W = W.contiguous()
+        cp = 0
+        if c is not None:
+            c = c.to(device=W.device, dtype=torch.float32).contiguous()
+            cp = c.data_ptr()
+        g = {"topk": SL_GATE_TOPK, "stat": SL_GATE_STAT, "fixed": SL_GATE_FIXED}[gate]
+        param = s_keep if g == SL_GATE_STAT else (tau if g == SL_GATE_FIXED else 0.0)
+        self.m, self.n, self.max_batch, self.device = m, n, max_batch, W.device
+        self.handle = sparse_linear_init(W.data_ptr(), self.w_dtype, lay, m, n, cp, g, K, param,
+                                         max_batch, torch.cuda.current_stream(W.device).cuda_stream)
+
+    def _stream(self):
+        return self._torch.cuda.current_stream(self.device).cuda_stream
+
+    def _out(self, B, y, y_dtype):
+        torch = self._torch
+        if y is None:
+            y = torch.empty((B, self.m), dtype=y_dtype, device=self.device)
+        return y
+
+    def forward(self, x, y=None, y_dtype=None, mask: bool = False, count: bool = False,
+                thresh: bool = False):
+        torch = self._torch
+        if x.dtype != self.dtype or not x.is_cuda or not x.is_contiguous():
+            raise ValueError("x must be a contiguous device tensor of W's dtype")
+        B = 1 if x.dim() == 1 else x.shape[0]
+        y_dtype = torch.float32 if y_dtype is None else y_dtype
+        y = self._out(B, y, y_dtype)
+        mk = torch.empty((B, self.n), dtype=torch.uint8, device=self.device) if mask else None
+        ct = torch.empty((B,), dtype=torch.int32, device=self.device) if count else None
+        th = torch.empty((B,), dtype=torch.float64, device=self.device) if thresh else None
+        sparse_linear_forward(self.handle, x.data_ptr(), B, y.data_ptr(),
+                              SL_BF16 if y.dtype == torch.bfloat16 else SL_F32,
+                              mk.data_ptr() if mk is not None else 0,
+                              ct.data_ptr() if ct is not None else 0,
+                              th.data_ptr() if th is not None else 0, self._stream())
+        return {"y": y, "mask": mk, "count": ct, "thresh": th}
+
+    def forward_dense(self, x, y=None, y_dtype=None):
+        torch = self._torch
+        B = 1 if x.dim() == 1 else x.shape[0]
+        y_dtype = torch.float32 if y_dtype is None else y_dtype
+        y = self._out(B, y, y_dtype)
+        sparse_linear_forward_dense(self.handle, x.data_ptr(), B, y.data_ptr(),
+                                    SL_BF16 if y.dtype == torch.bfloat16 else SL_F32, self._stream())
+        return y
+
+    def norms(self):
+        c = self._torch.empty((self.n,), dtype=self._torch.float32, device=self.device)
+        sparse_linear_get_norms(self.handle, c.data_ptr(), self._stream())
+        return c
+
+    def set_plan(self, rows_per_tile: int = 0, splits: int = 0):
+        sparse_linear_set_plan(self.handle, rows_per_tile, splits)
+
+    def timing(self, on: bool):
+        sparse_linear_timing_enable(self.handle, on)
+
+    def timing_read(self):
+        return sparse_linear_timing_read(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            sparse_linear_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,397 @@
+// Host runtime and C ABI of the weight-informed activation-sparse linear
+// layer: argument validation, handle-owned device buffers, the host-side
+// Phi^-1 for the statistical gate, launch planning and error mapping.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sl_status fail(sl_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+sl_status hip_fail(hipError_t e, const char* what) {
+  const sl_status st = (e == hipErrorOutOfMemory) ? SL_ERR_OOM : SL_ERR_HIP;
+  return fail(st, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define SL_HIP(expr)                                \
+  do {                                              \
+    hipError_t e_ = (expr);                         \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr); \
+  } while (0)
+
+// Phi^-1(p), Wichura's AS241 (PPND16), Applied Statistics 37 (1988) 477-484:
+// a rational approximation in r = 0.180625 - q^2 for |p - 1/2| <= 0.425, and in
+// r = sqrt(-log(min(p, 1-p))) (shifted by 1.6 or 5) in the tails, evaluated
+// in nested (Horner) form as published, in fp64, without fused multiply-add.
+double as241(double p) {
+  const double q = p - 0.5;
+  if (fabs(q) <= 0.425) {
+    const double r = 0.180625 - q * q;
+    const double num =
+        (((((((2.5090809287301226727e+3 * r + 3.3430575583588128105e+4) * r + 6.7265770927008700853e+4) * r +
+             4.5921953931549871457e+4) * r + 1.3731693765509461125e+4) * r + 1.9715909503065514427e+3) * r +
+          1.3314166789178437745e+2) * r + 3.3871328727963666080e+0) * q;
+    const double den =
+        ((((((5.2264952788528545610e+3 * r + 2.8729085735721942674e+4) * r + 3.9307895800092710610e+4) * r +
+             2.1213794301586595867e+4) * r + 5.3941960214247511077e+3) * r + 6.8718700749205790830e+2) * r +
+          4.2313330701600911252e+1) * r + 1.0;
+    return num / den;
+  }
+  double r = (q <= 0.0) ? p : 1.0 - p;
+  r = sqrt(-log(r));
+  double num, den;
+  if (r <= 5.0) {
+    r = r - 1.6;
+    num = (((((((7.74545014278341407640e-4 * r + 2.27238449892691845833e-2) * r + 2.41780725177450611770e-1) * r +
+               1.27045825245236838258e+0) * r + 3.64784832476320460504e+0) * r + 5.76949722146069140550e+0) * r +
+            4.63033784615654529590e+0) * r + 1.42343711074968357734e+0);
+    den = (((((((1.05075007164441684324e-9 * r + 5.47593808499534494600e-4) * r + 1.51986665636164571966e-2) * r +
+               1.48103976427480074590e-1) * r + 6.89767334985100004550e-1) * r + 1.67638483018380384940e+0) * r +
+            2.05319162663775882187e+0) * r + 1.0);
+  } else {
+    r = r - 5.0;
+    num = (((((((2.01033439929228813265e-7 * r + 2.71155556874348757815e-5) * r + 1.24266094738807843860e-3) * r +
+               2.65321895265761230930e-2) * r + 2.96560571828504891230e-1) * r + 1.78482653991729133580e+0) * r +
+            5.46378491116411436990e+0) * r + 6.65790464350110377720e+0);
+    den = (((((((2.04426310338993978564e-15 * r + 1.42151175831644588870e-7) * r + 1.84631831751005468180e-5) * r +
+               7.86869131145613259100e-4) * r + 1.48753612908506148525e-2) * r + 1.36929880922735805310e-1) * r +
+            5.99832206555887937690e-1) * r + 1.0);
+  }
+  double x = num / den;
+  if (q < 0.0) x = -x;
+  return x;
+}
+
+size_t dtype_size(sl_dtype d) { return d == SL_BF16 ? 2 : 4; }
+
+int vec_elems(sl_dtype d) { return d == SL_BF16 ? 8 : 4; }
+
+// Upper bound on the splits any plan may use (chunks of >= 32 inputs).
+int max_splits(int64_t n) { return (int)std::min<int64_t>(sl::kMaxSplits, (n + 31) / 32); }
+
+// Expected number of kept inputs, used to size the split count.
+int64_t expected_kept(const sl_linear* h, bool dense) {
+  if (dense) return h->n;
+  switch (h->gate) {
+    case SL_GATE_TOPK: return h->K;
+    case SL_GATE_STAT: return (int64_t)ceil(h->s_keep * (double)h->n);
+    default: return h->n / 2;
+  }
+}
+
+sl::Plan make_plan(const sl_linear* h, bool dense) {
+  sl::Plan p;
+  const int vec = vec_elems(h->wdt);
+  int lpc;
+  if (h->plan_rows > 0) {
+    lpc = h->plan_rows / vec;
+  } else if (h->m >= 8192) {
+    lpc = 64;
+  } else if (h->m >= 2048) {
+    lpc = 32;
+  } else {
+    lpc = 16;
+  }
+  lpc = std::max(16, std::min(64, lpc));
+  p.lpc = lpc;
+  p.rows = lpc * vec;
+  p.tiles = (int)((h->m + p.rows - 1) / p.rows);
+  p.unroll = 4;
+  const int64_t n = h->n;
+  int splits;
+  if (h->plan_splits > 0) {
+    splits = h->plan_splits;
+  } else {
+    const int64_t kept = std::max<int64_t>(1, expected_kept(h, dense));
+    splits = (int)std::max<int64_t>(1, 2048 / p.tiles);
+    splits = (int)std::min<int64_t>(splits, std::max<int64_t>(1, kept / 24));
+  }
+  splits = std::min(splits, max_splits(n));
+  splits = std::max<int>(splits, (int)((n + sl::kMaxChunk - 1) / sl::kMaxChunk));
+  p.chunk = (int)((n + splits - 1) / splits);
+  p.splits = (int)((n + p.chunk - 1) / p.chunk);
+  return p;
+}
+
+sl_status check_device(const sl_linear* h) {
+  int dev = -1;
+  SL_HIP(hipGetDevice(&dev));
+  if (dev != h->device) return fail(SL_ERR_ARG, "handle belongs to device %d, current device is %d", h->device, dev);
+  return SL_OK;
+}
+
+void free_handle(sl_linear* h) {
+  if (!h) return;
+  (void)hipFree(h->Wt);
+  (void)hipFree(h->c);
+  (void)hipFree(h->gout);
+  (void)hipFree(h->partials);
+  (void)hipFree(h->ctr);
+  (void)hipFree(h->upartials);
+  (void)hipFree(h->uctr);
+  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
+  delete h;
+}
+
+sl_status record(sl_linear* h, int slot, hipStream_t s) {
+  if (!h->timing) return SL_OK;
+  const size_t need = h->ev_used + 1;
+  while (h->ev.size() < need) {
+    hipEvent_t e;
+    SL_HIP(hipEventCreate(&e));
+    h->ev.push_back(e);
+  }
+  (void)slot;
+  SL_HIP(hipEventRecord(h->ev[h->ev_used], s));
+  h->ev_used++;
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_linear_strerror(sl_status s) {
+  switch (s) {
+    case SL_OK: return "success";
+    case SL_ERR_ARG: return "invalid argument";
+    case SL_ERR_UNSUPPORTED: return "unsupported shape or alignment";
+    case SL_ERR_OOM: return "device allocation failed";
+    case SL_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* sparse_linear_last_error(void) { return g_last_error.c_str(); }
+
+double sparse_linear_normal_quantile(double p) {
+  if (!(p > 0.0 && p < 1.0)) return NAN;
+  return as241(p);
+}
+
+sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl_layout w_layout, int64_t m,
+                             int64_t n, const float* c, sl_gate gate, int64_t K, double s_keep,
+                             int32_t max_batch, void* stream) {
+  try {
+    g_last_error.clear();
+    if (out == nullptr) return fail(SL_ERR_ARG, "out is NULL");
+    if (W == nullptr) return fail(SL_ERR_ARG, "W is NULL");
+    if (w_dtype != SL_F32 && w_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad w_dtype %d", (int)w_dtype);
+    if (w_layout != SL_W_ROWMAJOR_OUT_IN && w_layout != SL_W_COLMAJOR)
+      return fail(SL_ERR_ARG, "bad w_layout %d", (int)w_layout);
+    if (m < 1 || n < 1) return fail(SL_ERR_ARG, "m and n must be >= 1 (m=%lld n=%lld)", (long long)m, (long long)n);
+    if (n > SL_MAX_N) return fail(SL_ERR_UNSUPPORTED, "n=%lld exceeds %d", (long long)n, SL_MAX_N);
+    if (m > (1 << 21)) return fail(SL_ERR_UNSUPPORTED, "m=%lld exceeds 2^21", (long long)m);
+    if (m % vec_elems(w_dtype) != 0)
+      return fail(SL_ERR_UNSUPPORTED, "m=%lld must be a multiple of %d for this dtype", (long long)m,
+                  vec_elems(w_dtype));
+    if (max_batch < 1 || max_batch > SL_MAX_BATCH)
+      return fail(SL_ERR_ARG, "max_batch=%d outside [1, %d]", (int)max_batch, SL_MAX_BATCH);
+    switch (gate) {
+      case SL_GATE_TOPK:
+        if (K < 0 || K > n) return fail(SL_ERR_ARG, "K=%lld outside [0, n=%lld]", (long long)K, (long long)n);
+        break;
+      case SL_GATE_STAT:
+        if (!(s_keep > 0.0 && s_keep < 1.0)) return fail(SL_ERR_ARG, "s_keep=%g outside (0, 1)", s_keep);
+        break;
+      case SL_GATE_FIXED:
+        if (!(s_keep >= 0.0) || !isfinite(s_keep) || s_keep > 3.0e38)
+          return fail(SL_ERR_ARG, "tau=%g must be finite and >= 0", s_keep);
+        break;
+      default:
+        return fail(SL_ERR_ARG, "bad gate %d", (int)gate);
+    }
+    int dev = -1;
+    SL_HIP(hipGetDevice(&dev));
+    hipStream_t s = (hipStream_t)stream;
+
+    sl_linear* h = new (std::nothrow) sl_linear();
+    if (!h) return fail(SL_ERR_OOM, "host allocation failed");
+    h->device = dev;
+    h->m = m;
+    h->n = n;
+    h->wdt = w_dtype;
+    h->gate = gate;
+    h->K = (gate == SL_GATE_TOPK) ? K : 0;
+    h->s_keep = s_keep;
+    h->max_batch = max_batch;
+    if (gate == SL_GATE_STAT) h->z = as241(1.0 - s_keep);
+    if (gate == SL_GATE_FIXED) h->tau = (float)s_keep;
+
+    auto cleanup_fail = [&](hipError_t e, const char* what) {
+      free_handle(h);
+      return hip_fail(e, what);
+    };
+    hipError_t e;
+    const size_t wbytes = (size_t)m * (size_t)n * dtype_size(w_dtype);
+    if ((e = hipMalloc(&h->Wt, wbytes)) != hipSuccess) return cleanup_fail(e, "hipMalloc(W)");
+    if ((e = hipMalloc(&h->c, (size_t)n * sizeof(float))) != hipSuccess) return cleanup_fail(e, "hipMalloc(c)");
+    if ((e = hipMalloc(&h->gout, (size_t)max_batch * sizeof(sl::GateOut))) != hipSuccess)
+      return cleanup_fail(e, "hipMalloc(gate)");
+    const size_t part = (size_t)max_splits(n) * (size_t)m * sizeof(float);
+    if ((e = hipMalloc(&h->partials, part)) != hipSuccess) return cleanup_fail(e, "hipMalloc(partials)");
+    h->ctr_len = (m + 63) / 64 + 1;
+    if ((e = hipMalloc(&h->ctr, (size_t)h->ctr_len * sizeof(uint32_t))) != hipSuccess)
+      return cleanup_fail(e, "hipMalloc(counters)");
+    if ((e = hipMemsetAsync(h->ctr, 0, (size_t)h->ctr_len * sizeof(uint32_t), s)) != hipSuccess)
+      return cleanup_fail(e, "hipMemsetAsync(counters)");
+
+    if (w_layout == SL_W_ROWMAJOR_OUT_IN) {
+      if ((e = sl::launch_repack(W, w_dtype, m, n, h->Wt, s)) != hipSuccess) return cleanup_fail(e, "repack");
+    } else {
+      if ((e = hipMemcpyAsync(h->Wt, W, wbytes, hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return cleanup_fail(e, "hipMemcpyAsync(W)");
+    }
+    if (c != nullptr) {
+      if ((e = hipMemcpyAsync(h->c, c, (size_t)n * sizeof(float), hipMemcpyDeviceToDevice, s)) != hipSuccess)
+        return cleanup_fail(e, "hipMemcpyAsync(c)");
+    } else {
+      if ((e = sl::launch_norms(h->Wt, w_dtype, m, n, h->c, s)) != hipSuccess) return cleanup_fail(e, "norms");
+    }
+    {
+      // Every slot starts as "keep nothing"; a fixed threshold is known now, so the
+      // product kernel can run without a gate launch.
+      std::vector<sl::GateOut> g0(max_batch);
+      for (auto& g : g0) {
+        g.kthr = 0xffffffffu;
+        g.jlast = -1;
+        g.count = 0;
+        g.pad = 0;
+        g.thresh = 0.0;
+        if (gate == SL_GATE_FIXED) {
+          uint32_t bits;
+          memcpy(&bits, &h->tau, sizeof(bits));
+          g.kthr = bits & 0x7fffffffu;
+          g.thresh = (double)h->tau;
+        }
+      }
+      if ((e = hipMemcpyAsync(h->gout, g0.data(), g0.size() * sizeof(sl::GateOut), hipMemcpyHostToDevice, s)) !=
+          hipSuccess)
+        return cleanup_fail(e, "hipMemcpyAsync(gate)");
+      if ((e = hipStreamSynchronize(s)) != hipSuccess) return cleanup_fail(e, "hipStreamSynchronize");
+    }
+    *out = h;
+    return SL_OK;
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in init");
+  }
+}
+
+static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                              uint8_t* mask_out, int32_t* count_out, double* thresh_out, void* stream,
+                              bool dense) {
+  g_last_error.clear();
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  if (x == nullptr || y == nullptr) return fail(SL_ERR_ARG, "x and y must be non-NULL");
+  if (B < 1 || B > h->max_batch) return fail(SL_ERR_ARG, "B=%d outside [1, max_batch=%d]", (int)B, h->max_batch);
+  if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
+  if (B > 1) return fail(SL_ERR_UNSUPPORTED, "batched forward (B > 1) is not built yet");
+  sl_status st = check_device(h);
+  if (st != SL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+
+  const bool need_gate = !dense && (h->gate != SL_GATE_FIXED || mask_out || count_out || thresh_out);
+  const sl::Plan plan = make_plan(h, dense);
+  if ((st = record(h, 0, s)) != SL_OK) return st;
+  if (need_gate) SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, s));
+  if ((st = record(h, 1, s)) != SL_OK) return st;
+  SL_HIP(sl::launch_product(h, plan, x, dense, y, y_dtype, s));
+  if ((st = record(h, 2, s)) != SL_OK) return st;
+  return SL_OK;
+}
+
+sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                                uint8_t* mask_out, int32_t* count_out, double* thresh_out, void* stream) {
+  try {
+    return forward_impl(h, x, B, y, y_dtype, mask_out, count_out, thresh_out, stream, false);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward");
+  }
+}
+
+sl_status sparse_linear_forward_dense(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                                      void* stream) {
+  try {
+    return forward_impl(h, x, B, y, y_dtype, nullptr, nullptr, nullptr, stream, true);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_dense");
+  }
+}
+
+sl_status sparse_linear_get_norms(sl_handle h, float* c_out, void* stream) {
+  if (h == nullptr || c_out == nullptr) return fail(SL_ERR_ARG, "NULL argument");
+  sl_status st = check_device(h);
+  if (st != SL_OK) return st;
+  SL_HIP(hipMemcpyAsync(c_out, h->c, (size_t)h->n * sizeof(float), hipMemcpyDeviceToDevice, (hipStream_t)stream));
+  return SL_OK;
+}
+
+sl_status sparse_linear_destroy(sl_handle h) {
+  free_handle(h);
+  return SL_OK;
+}
+
+sl_status sparse_linear_timing_enable(sl_handle h, int32_t on) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  h->timing = (on != 0);
+  h->ev_used = 0;
+  h->acc_gate_ms = h->acc_prod_ms = 0.0;
+  h->acc_fwd = 0;
+  return SL_OK;
+}
+
+sl_status sparse_linear_timing_read(sl_handle h, double* gate_ms, double* product_ms, int64_t* forwards) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  double g = 0.0, p = 0.0;
+  const size_t nf = h->ev_used / 3;
+  for (size_t f = 0; f < nf; ++f) {
+    float a = 0.f, b = 0.f;
+    SL_HIP(hipEventSynchronize(h->ev[3 * f + 2]));
+    SL_HIP(hipEventElapsedTime(&a, h->ev[3 * f], h->ev[3 * f + 1]));
+    SL_HIP(hipEventElapsedTime(&b, h->ev[3 * f + 1], h->ev[3 * f + 2]));
+    g += a;
+    p += b;
+  }
+  if (gate_ms) *gate_ms = g;
+  if (product_ms) *product_ms = p;
+  if (forwards) *forwards = (int64_t)nf;
+  h->ev_used = 0;
+  return SL_OK;
+}
+
+sl_status sparse_linear_set_plan(sl_handle h, int32_t rows_per_tile, int32_t splits) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  const int vec = vec_elems(h->wdt);
+  if (rows_per_tile != 0) {
+    const int lpc = rows_per_tile / vec;
+    if (rows_per_tile % vec != 0 || (lpc != 16 && lpc != 32 && lpc != 64))
+      return fail(SL_ERR_ARG, "rows_per_tile=%d must be 16, 32 or 64 times %d", (int)rows_per_tile, vec);
+  }
+  if (splits < 0 || splits > max_splits(h->n)) return fail(SL_ERR_ARG, "splits=%d outside [0, %d]", (int)splits, max_splits(h->n));
+  h->plan_rows = rows_per_tile;
+  h->plan_splits = splits;
+  return SL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Internal declarations shared by the host runtime and the gfx950 kernels of
+// the weight-informed activation-sparse linear layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "../../include/sparse_linear.h"
+
+namespace sl {
+
+// Per-token result of the gate. The kept set is
+//   { j : key_j > kthr  or  (key_j == kthr and j <= jlast) }
+// where key_j is the fp32 bit pattern of score_j = |x_j * c_j| (non-negative,
+// so unsigned order equals numeric order). Every gate mode reduces to this
+// form: top-K puts the K-th largest key in kthr and the index of the last kept
+// tie in jlast; a threshold t >= 0 becomes kthr = bits(round_down_f32(t)),
+// jlast = -1.
+struct GateOut {
+  uint32_t kthr;
+  int32_t jlast;
+  int32_t count;
+  int32_t pad;
+  double thresh;
+};
+static_assert(sizeof(GateOut) == 24, "GateOut layout");
+
+// Scratch limits of the single-token product kernel.
+constexpr int kMaxSplits = 1024;   // K-splits per row tile
+constexpr int kMaxChunk = 1024;    // inputs examined per workgroup
+
+struct Plan {
+  int lpc;     // lanes per column run (16, 32 or 64)
+  int rows;    // rows per tile (lpc * elements per 16-byte load)
+  int tiles;   // ceil(m / rows)
+  int splits;  // input chunks
+  int chunk;   // inputs per chunk
+  int unroll;  // columns in flight per lane group
+};
+
+// Matrix-core (union) product plan.
+struct UnionPlan {
+  int tiles;   // row tiles of 64 rows
+  int splits;  // input chunks
+  int chunk;   // inputs per chunk (multiple of 32, <= 256)
+};
+
+}  // namespace sl
+
+struct sl_linear {
+  int device = 0;
+  int64_t m = 0, n = 0;
+  sl_dtype wdt = SL_BF16;
+  sl_gate gate = SL_GATE_TOPK;
+  int64_t K = 0;
+  double s_keep = 0.0;
+  double z = 0.0;     // Phi^-1(fl(1 - s_keep)), STAT
+  float tau = 0.0f;   // FIXED
+  int max_batch = 1;
+
+  void* Wt = nullptr;           // column-major [n][m], wdt
+  float* c = nullptr;           // [n]
+  sl::GateOut* gout = nullptr;  // [max_batch]
+  float* partials = nullptr;    // [kMaxSplits * m] (single-token product)
+  uint32_t* ctr = nullptr;      // [tiles] arrival counters, self-resetting
+  int64_t ctr_len = 0;
+  float* upartials = nullptr;   // [usplits][max_batch][m] (union product)
+  int64_t upart_len = 0;
+  uint32_t* uctr = nullptr;     // [utiles]
+
+  int plan_rows = 0, plan_splits = 0;  // overrides (0 = automatic)
+
+  bool timing = false;
+  std::vector<hipEvent_t> ev;   // 3 per forward: start, after gate, after product
+  size_t ev_used = 0;
+  double acc_gate_ms = 0.0, acc_prod_ms = 0.0;
+  int64_t acc_fwd = 0;
+};
+
+namespace sl {
+
+// Launchers (each returns the launch's hipError_t).
+hipError_t launch_repack(const void* W, sl_dtype dt, int64_t m, int64_t n, void* Wt, hipStream_t s);
+hipError_t launch_norms(const void* Wt, sl_dtype dt, int64_t m, int64_t n, float* c, hipStream_t s);
+hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_out,
+                       int32_t* count_out, double* thresh_out, hipStream_t s);
+hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, bool dense, void* y,
+                          sl_dtype ydt, hipStream_t s);
+hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,
+                                bool dense, void* y, sl_dtype ydt, hipStream_t s);
+
+}  // namespace sl

@@ -1,0 +1,171 @@
+/*
+ * sparse_linear.h -- C ABI of the weight-informed activation-sparse linear
+ * layer for LLM decode on AMD Instinct MI355X (gfx950).
+ *
+ * What one forward computes, per token b (pages cited by title and section):
+ *
+ *   score_j = |x_j * c_j|,  c_j = L2 norm of column j of W
+ *       (WINA article, arXiv:2505.19427, section 一: the gate ranks inputs by
+ *        hidden-state magnitude times the column norm of the weight they meet)
+ *   keep    = the K largest scores, ties to the lower index   (SL_GATE_TOPK,
+ *             WINA article, section 一: top-K binary gate)
+ *           | score > t, t = mu + sigma * Phi^-1(1 - s)        (SL_GATE_STAT,
+ *             Spark Transformer article, section 2.2: statistical top-k with
+ *             mean and population variance of the score vector)
+ *   y       = sum over kept j of x_j * W[:, j]
+ *       (Spark Transformer article, section 3.1: the index-list product that
+ *        touches only the weight vectors of active inputs)
+ *
+ * Shapes: W is m x n (m outputs, n inputs), x is [B][n], y is [B][m].
+ *
+ * Memory: every pointer argument named "device" is device memory of the
+ * current HIP device; handles are bound to the device current at init.
+ * Streams are hipStream_t values passed as void* (NULL = the default stream).
+ *
+ * Errors: every argument check happens before anything is enqueued; on error
+ * nothing is launched and the out-parameters are untouched. HIP runtime
+ * failures map to SL_ERR_HIP. No C++ exception crosses this interface.
+ * sparse_linear_last_error() returns a message for the calling thread's most
+ * recent failure. NaN or Inf inside x or c is not detected: the mask is then
+ * unspecified and y propagates the NaN.
+ */
+#ifndef SPARSE_LINEAR_H
+#define SPARSE_LINEAR_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sl_linear* sl_handle; /* opaque, library-owned */
+
+typedef enum {
+  SL_OK = 0,
+  SL_ERR_ARG = 1,         /* invalid argument (null pointer, range)        */
+  SL_ERR_UNSUPPORTED = 2, /* valid but not supported (alignment, size)     */
+  SL_ERR_OOM = 3,         /* device allocation failed                      */
+  SL_ERR_HIP = 4          /* HIP runtime error (no device, launch failure) */
+} sl_status;
+
+typedef enum { SL_F32 = 0, SL_BF16 = 1 } sl_dtype;
+
+typedef enum {
+  SL_W_ROWMAJOR_OUT_IN = 0, /* W[i][j] at i*n + j: the torch nn.Linear layout */
+  SL_W_COLMAJOR = 1         /* W[i][j] at j*m + i: column j contiguous        */
+} sl_layout;
+
+typedef enum {
+  SL_GATE_TOPK = 0,  /* exact top-K of the scores                          */
+  SL_GATE_STAT = 1,  /* Gaussian-fit threshold, keep fraction s_keep        */
+  SL_GATE_FIXED = 2  /* calibrated per-layer threshold: keep score > tau    */
+} sl_gate;
+
+/* Limits of this build. */
+#define SL_MAX_N 32768     /* inputs per token (the gate keeps them in LDS) */
+#define SL_MAX_BATCH 16    /* tokens per forward                              */
+
+/*
+ * sparse_linear_init -- build a handle for one linear layer.
+ *
+ *   W        device, m*n elements of w_dtype in w_layout. Copied (and, for
+ *            SL_W_ROWMAJOR_OUT_IN, transposed) into handle-owned column-major
+ *            storage [n][m], so that the m weights that input j multiplies are
+ *            one contiguous run (the weight vector W[j] of the index-list
+ *            product, Spark Transformer article, section 3.1).
+ *   c        device fp32[n], the column norms, copied; or NULL, in which case
+ *            the library computes c_j = fp32(sqrt(sum_i W[i][j]^2)) with an
+ *            fp64 sum (WINA article, section 一). Values must be finite.
+ *   gate     SL_GATE_TOPK: K in [0, n] inputs kept per token.
+ *            SL_GATE_STAT: s_keep in (0, 1); z = Phi^-1(fl(1 - s_keep)) is
+ *            evaluated once here with Wichura's algorithm AS241.
+ *            SL_GATE_FIXED: s_keep carries tau >= 0 (rounded to fp32); the
+ *            gate keeps score > tau (a per-layer threshold of the kind the
+ *            WINA article, section 三, calibrates from hidden-state
+ *            distributions).
+ *   max_batch  1..SL_MAX_BATCH, the largest B forward will accept; sizes the
+ *            per-handle scratch.
+ *   stream   the stream the copies run on; init synchronizes it before
+ *            returning, so caller buffers may be freed afterwards.
+ *
+ * Requirements: m >= 1, 1 <= n <= SL_MAX_N; m % 8 == 0 for bf16 and m % 4 == 0
+ * for fp32 (16-byte column runs), else SL_ERR_UNSUPPORTED.
+ * Returns SL_ERR_HIP when no HIP device is usable.
+ */
+sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl_layout w_layout,
+                             int64_t m, int64_t n, const float* c, sl_gate gate, int64_t K,
+                             double s_keep, int32_t max_batch, void* stream);
+
+/*
+ * sparse_linear_forward -- y = W[:, keep] x[keep] for B tokens.
+ *
+ *   x          device [B][n], same dtype as W.
+ *   y          device [B][m] of y_dtype (fp32, or bf16 rounded to nearest even
+ *              from the fp32 accumulator).
+ *   mask_out   device uint8 [B][n] or NULL: 1 where input j was kept.
+ *   count_out  device int32 [B] or NULL: number of kept inputs.
+ *   thresh_out device double [B] or NULL: t (STAT), tau (FIXED) or the K-th
+ *              largest score (TOPK; +inf when K == 0).
+ *
+ * Each token's kept set depends only on that token. For B > 1 the library
+ * forms the union of the B masks and runs one matrix-core pass over the union
+ * columns, feeding zero for inputs a token did not keep.
+ * Asynchronous on `stream`; the caller keeps x, y and the optional outputs
+ * alive until the stream has completed. A handle's scratch is shared by its
+ * calls, so one handle must not run on two streams at once.
+ */
+sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                                uint8_t* mask_out, int32_t* count_out, double* thresh_out,
+                                void* stream);
+
+/*
+ * sparse_linear_forward_dense -- y = W x for B tokens with every input kept,
+ * run by the same product kernel as the sparse path over the identity index
+ * list (the dense baseline the sparse forward is compared against).
+ * Same argument rules as sparse_linear_forward.
+ */
+sl_status sparse_linear_forward_dense(sl_handle h, const void* x, int32_t B, void* y,
+                                      sl_dtype y_dtype, void* stream);
+
+/* Copy the handle's fp32 norm vector c into device fp32[n] (stream-ordered). */
+sl_status sparse_linear_get_norms(sl_handle h, float* c_out, void* stream);
+
+/* Release a handle. The handle's last stream must be idle. NULL is a no-op. */
+sl_status sparse_linear_destroy(sl_handle h);
+
+/* Static description of a status code. */
+const char* sparse_linear_strerror(sl_status s);
+
+/* Message for the calling thread's most recent failure ("" if none). */
+const char* sparse_linear_last_error(void);
+
+/*
+ * Phi^-1(p) for 0 < p < 1 by Wichura's AS241 (Applied Statistics 37, 1988),
+ * evaluated in fp64 on the host exactly as the STAT gate's init does. Returns
+ * NaN outside (0, 1). Host-only; needs no device.
+ */
+double sparse_linear_normal_quantile(double p);
+
+/*
+ * Kernel timing for measurement. When enabled (on != 0), each forward records
+ * HIP events around its gate kernel and its product kernel on the forward's
+ * stream; sparse_linear_timing_read() synchronizes on the recorded events and
+ * returns the summed durations in milliseconds and the number of forwards
+ * recorded since the last read (then resets). Off by default.
+ */
+sl_status sparse_linear_timing_enable(sl_handle h, int32_t on);
+sl_status sparse_linear_timing_read(sl_handle h, double* gate_ms, double* product_ms,
+                                    int64_t* forwards);
+
+/*
+ * Launch-shape override for tuning sweeps: rows_per_tile in {128, 256, 512}
+ * (0 = automatic) and splits >= 0 (0 = automatic) for the single-token product
+ * kernel. Takes effect on the next forward.
+ */
+sl_status sparse_linear_set_plan(sl_handle h, int32_t rows_per_tile, int32_t splits);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_LINEAR_H */

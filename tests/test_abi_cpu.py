@@ -1,0 +1,108 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol,
+validates arguments before touching a device, reports a missing device
+cleanly, and evaluates AS241 on the host bit for bit like the stdlib."""
+import ctypes
+import math
+import os
+import re
+import statistics
+
+import numpy as np
+import pytest
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sparse_linear.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(sparse_linear_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(slib):
+    L = slib.lib()
+    names = _declared()
+    assert len(names) >= 10
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(slib.EXPORTED) == names
+
+
+@pytest.mark.parametrize("p", [1e-300, 1e-30, 1e-12, 1e-4, 0.001, 0.01, 0.02425, 0.05, 0.075, 0.0749,
+                               0.0751, 0.1, 0.2, 0.3, 0.45, 0.5, 0.55, 0.7, 0.8, 0.9, 0.9249, 0.925,
+                               0.9251, 0.95, 0.975, 0.99, 0.9999, 1 - 1e-12])
+def test_host_quantile_bitwise_stdlib(slib, p):
+    got = slib.sparse_linear_normal_quantile(p)
+    want = statistics.NormalDist().inv_cdf(p)
+    assert got.hex() == want.hex()
+
+
+def test_host_quantile_dense_sweep(slib):
+    g = np.random.default_rng(41)
+    ps = np.concatenate([g.random(4000), np.exp(-g.uniform(0, 700, 1000)), 1 - np.exp(-g.uniform(2, 36, 500))])
+    nd = statistics.NormalDist()
+    bad = [p for p in ps.tolist() if 0 < p < 1 and slib.sparse_linear_normal_quantile(p) != nd.inv_cdf(p)]
+    assert bad == []
+    # the STAT gate's z for the keep fractions used by the workloads
+    for s in (0.05, 0.1, 0.15, 0.3, 0.5):
+        assert slib.sparse_linear_normal_quantile(1.0 - s) == nd.inv_cdf(1.0 - s)
+
+
+def test_host_quantile_outside_domain(slib):
+    for p in (0.0, 1.0, -0.5, 2.0, float("nan")):
+        assert math.isnan(slib.sparse_linear_normal_quantile(p))
+
+
+def _init(slib, W=1, dt=1, lay=0, m=64, n=32, c=0, gate=0, K=8, s=0.0, mb=1):
+    h = ctypes.c_void_p()
+    st = slib.lib().sparse_linear_init(ctypes.byref(h), W or None, dt, lay, m, n, c or None, gate, K, s, mb, None)
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=0), 1),
+    (dict(dt=7), 1),
+    (dict(lay=5), 1),
+    (dict(m=0), 1),
+    (dict(n=0), 1),
+    (dict(n=32769), 2),
+    (dict(m=12), 2),            # bf16 needs m % 8 == 0
+    (dict(dt=0, m=6), 2),       # fp32 needs m % 4 == 0
+    (dict(K=-1), 1),
+    (dict(K=33), 1),
+    (dict(gate=1, s=0.0), 1),
+    (dict(gate=1, s=1.0), 1),
+    (dict(gate=1, s=float("nan")), 1),
+    (dict(gate=2, s=-1.0), 1),
+    (dict(gate=9), 1),
+    (dict(mb=0), 1),
+    (dict(mb=17), 1),
+])
+def test_init_rejects_bad_arguments(slib, kw, status):
+    st, h = _init(slib, **kw)
+    assert st == status, slib.sparse_linear_last_error()
+    assert h.value is None
+    assert slib.sparse_linear_last_error() != ""
+
+
+def test_init_without_device_reports_hip_error(slib):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a device is present")
+    st, h = _init(slib)
+    assert st == 4
+    assert h.value is None
+
+
+def test_forward_rejects_null_handle_and_pointers(slib):
+    L = slib.lib()
+    assert L.sparse_linear_forward(None, 1, 1, 1, 0, None, None, None, None) == 1
+    assert L.sparse_linear_forward_dense(None, 1, 1, 1, 0, None) == 1
+    assert L.sparse_linear_get_norms(None, 1, None) == 1
+    assert L.sparse_linear_destroy(None) == 0
+    assert L.sparse_linear_set_plan(None, 0, 0) == 1
+
+
+def test_strerror(slib):
+    assert slib.sparse_linear_strerror(0) == "success"
+    assert slib.sparse_linear_strerror(2) == "unsupported shape or alignment"
+    assert slib.sparse_linear_strerror(99) == "unknown status"

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Masks, counts and thresholds must match bit for bit; y within relative L2
+2e-3 of the fp64 oracle. Inputs are the seeded workloads (full layer sizes
+where the oracle can follow, sampled output rows where it cannot compute
+every row quickly) plus ragged and degenerate edge cases.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from parity_util import REL_L2_TOL, check_token, gate_kwargs, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fas(slib):
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return slib
+
+
+def _layer(fas, W, c, mode, K=None, s_keep=None, tau=None, layout="rowmajor", max_batch=1, pass_c=True):
+    Wd = to_dev(W if layout == "rowmajor" else np.ascontiguousarray(W.T), torch)
+    cd = to_dev(c, torch) if pass_c else None
+    return fas.SparseLinear(Wd, c=cd, layout=layout, max_batch=max_batch,
+                            **gate_kwargs(mode, K=K, s_keep=s_keep, tau=tau))
+
+
+def _fwd(layer, x, **kw):
+    out = layer.forward(to_dev(x, torch)[None, :], mask=True, count=True, thresh=True, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+# ---------------------------------------------------------------- config 1
+def test_tiny_config_all_tokens(fas):
+    cfg = wl.CONFIGS[1]
+    W = wl.weight(1, 0)
+    c = oracle.column_norms(W)
+    K = wl.k_from_sparsity(256, 0.5)
+    layer = _layer(fas, W, c, "topk", K=K)
+    for t in range(cfg.tokens):
+        x = wl.token(1, 0, t)
+        print(f"[tiny] token {t}", flush=True)
+        check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, ctx="tiny")
+
+
+def test_tiny_bf16_output(fas):
+    W = wl.weight(1, 0)
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "topk", K=128)
+    x = wl.token(1, 0, 3)
+    out = _fwd(layer, x, y_dtype=torch.bfloat16)
+    assert out["y"].dtype == torch.bfloat16
+    # bf16 rounding of y adds up to 2^-9 relative per element
+    check_token(out, 0, W, c, x, "topk", K=128, tol=REL_L2_TOL, ctx="tiny-bf16y")
+
+
+# ---------------------------------------------------------------- config 2
+@pytest.fixture(scope="module")
+def llama_down():
+    W = wl.weight(2, 0)
+    return W, oracle.column_norms(W)
+
+
+@pytest.mark.parametrize("sparsity", [0.5, 0.65])
+def test_llama7b_down_full_size(fas, llama_down, sparsity):
+    W, c = llama_down
+    K = wl.k_from_sparsity(W.shape[1], sparsity)
+    layer = _layer(fas, W, c, "topk", K=K)
+    rows = np.random.default_rng(7).choice(W.shape[0], 96, replace=False)
+    for t in range(12):
+        x = wl.token(2, 0, t)
+        print(f"[llama-down p={sparsity}] token {t}", flush=True)
+        full = t < 2  # the whole y for two tokens, sampled rows for the rest
+        check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=None if full else rows, ctx="llama-down")
+    layer.close()
+
+
+def test_llama7b_down_plans(fas, llama_down):
+    """Every launch shape gives the same masks and an oracle-close y."""
+    W, c = llama_down
+    K = wl.k_from_sparsity(W.shape[1], 0.65)
+    layer = _layer(fas, W, c, "topk", K=K)
+    x = wl.token(2, 0, 100)
+    rows = np.arange(0, W.shape[0], 37)
+    for rpt in (128, 256, 512):
+        for splits in (1, 7, 64, 300):
+            print(f"[plan] rows {rpt} splits {splits}", flush=True)
+            layer.set_plan(rpt, splits)
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=rows, ctx=f"plan {rpt}/{splits}")
+    layer.close()
+
+
+# ---------------------------------------------------------------- STAT gate (config 4 shapes)
+@pytest.mark.parametrize("linear", [0, 2])
+def test_phi4_stat_gate_full_size(fas, linear):
+    W = wl.weight(4, linear)
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "stat", s_keep=0.10)
+    rows = np.random.default_rng(9).choice(W.shape[0], 64, replace=False)
+    for t in range(8):
+        x = wl.token(4, linear, t)
+        print(f"[phi4 stat linear {linear}] token {t}", flush=True)
+        check_token(_fwd(layer, x), 0, W, c, x, "stat", s_keep=0.10, rows=rows, ctx="phi4-stat")
+    layer.close()
+
+
+# ---------------------------------------------------------------- config 3 (seven linears)
+def test_llama3_block_linears(fas):
+    ps = wl.component_sparsities(3)
+    for li, lin in enumerate(wl.CONFIGS[3].linears):
+        W = wl.weight(3, li)
+        c = oracle.column_norms(W)
+        K = wl.k_from_sparsity(lin.n, round(ps[li], 6))
+        layer = _layer(fas, W, c, "topk", K=K)
+        rows = np.random.default_rng(li).choice(lin.m, 48, replace=False)
+        for t in range(3):
+            x = wl.token(3, li, t)
+            print(f"[llama3 {lin.name}] token {t} K={K}", flush=True)
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=rows, ctx=f"llama3-{lin.name}")
+        layer.close()
+        del W
+
+
+# ---------------------------------------------------------------- edge cases
+EDGE_SHAPES = [(8, 1), (136, 1000), (520, 2049), (1032, 300), (64, 4100)]
+
+
+@pytest.mark.parametrize("m,n", EDGE_SHAPES)
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_ragged_shapes_topk(fas, m, n, dtype):
+    W = wl.random_matrix(m * 7 + n, m, n, dtype)
+    c = oracle.column_norms(W)
+    g = np.random.default_rng(m + n)
+    for K in sorted({0, 1, n // 3, n - 1, n}):
+        if K < 0:
+            continue
+        layer = _layer(fas, W, c, "topk", K=K)
+        for t, kind in enumerate(["normal", "ties"]):
+            x = wl.random_tokens(m + n + t, 1, n, dtype, kind)[0]
+            print(f"[ragged {dtype} {m}x{n}] K={K} {kind}", flush=True)
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, ctx=f"ragged {m}x{n} K={K} {kind}")
+        layer.close()
+    del g
+
+
+@pytest.mark.parametrize("s_keep", [0.02, 0.1, 0.5, 0.9])
+def test_stat_gate_small(fas, s_keep):
+    m, n = 264, 3000
+    W = wl.random_matrix(5, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "stat", s_keep=s_keep)
+    for t, kind in enumerate(["laplace", "normal", "ties"]):
+        x = wl.random_tokens(50 + t, 1, n, "bf16", kind)[0]
+        check_token(_fwd(layer, x), 0, W, c, x, "stat", s_keep=s_keep, ctx=f"stat s={s_keep} {kind}")
+    layer.close()
+
+
+def test_stat_gate_constant_scores(fas):
+    # every score equal: sigma = 0, t = mu, nothing kept, y = 0
+    m, n = 64, 500
+    W = wl.random_matrix(6, m, n, "f32")
+    c = np.ones(n, np.float32)
+    layer = _layer(fas, W, c, "stat", s_keep=0.1)
+    x = np.full(n, -0.75, np.float32)
+    out = _fwd(layer, x)
+    check_token(out, 0, W, c, x, "stat", s_keep=0.1, ctx="stat-constant")
+    assert int(out["count"][0]) == 0 and float(out["thresh"][0]) == 0.75
+    assert torch.count_nonzero(out["y"]).item() == 0
+
+
+@pytest.mark.parametrize("tau", [0.0, 0.01, 0.05, 1e9])
+def test_fixed_threshold(fas, tau):
+    m, n = 128, 2000
+    W = wl.random_matrix(8, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "fixed", tau=tau)
+    x = wl.random_tokens(9, 1, n, "bf16", "laplace")[0]
+    check_token(_fwd(layer, x), 0, W, c, x, "fixed", tau=tau, ctx=f"fixed tau={tau}")
+    # without requested outputs the gate kernel is skipped; y must not change
+    y2 = layer.forward(to_dev(x, torch)[None, :])["y"]
+    torch.cuda.synchronize()
+    ref = oracle.forward(W, c, x, "fixed", tau=tau)
+    assert rel_l2(y2[0].cpu().numpy(), ref["y"]) <= REL_L2_TOL
+    layer.close()
+
+
+# ---------------------------------------------------------------- identities
+def test_topk_all_equals_dense_kernel(fas):
+    m, n = 1024, 4096
+    W = wl.random_matrix(10, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "topk", K=n)
+    x = to_dev(wl.random_tokens(11, 1, n, "bf16")[0], torch)[None, :]
+    ys = layer.forward(x)["y"]
+    yd = layer.forward_dense(x)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, yd)
+    ref = oracle.sparse_product(W, wl.random_tokens(11, 1, n, "bf16")[0], np.arange(n))
+    assert rel_l2(yd[0].cpu().numpy(), ref) <= REL_L2_TOL
+    layer.close()
+
+
+def test_one_hot_input_returns_column(fas):
+    m, n = 512, 777
+    W = wl.random_matrix(12, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "topk", K=5)
+    for j in (0, 1, 400, n - 1):
+        x = np.zeros(n, np.float32)
+        x[j] = 1.0
+        xb = wl.f32_to_bf16_bits(x)
+        out = _fwd(layer, xb)
+        want = oracle.as_f64(W)[:, j]
+        np.testing.assert_array_equal(out["y"][0].cpu().numpy().astype(np.float64), want)
+        assert out["mask"][0].cpu().numpy().sum() == 5
+    layer.close()
+
+
+def test_orthogonal_error_identity_on_gpu(fas):
+    g = np.random.default_rng(13)
+    m, n, K = 512, 256, 100
+    Q, _ = np.linalg.qr(g.standard_normal((m, n)))
+    d = np.exp(g.uniform(np.log(0.1), np.log(10.0), n))
+    W = (Q * d).astype(np.float32)
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "topk", K=K)
+    x = g.standard_normal(n).astype(np.float32)
+    out = _fwd(layer, x)
+    yd = layer.forward_dense(to_dev(x, torch)[None, :])
+    torch.cuda.synchronize()
+    diff = (yd[0].double() - out["y"][0].double()).cpu().numpy()
+    mask = out["mask"][0].cpu().numpy().astype(bool)
+    s = oracle.scores(x, c).astype(np.float64)
+    closed = np.sum(s[~mask] ** 2)
+    assert abs(np.sum(diff ** 2) - closed) <= 1e-4 * closed
+    layer.close()
+
+
+def test_library_norms_and_colmajor_layout(fas):
+    m, n = 2056, 1500
+    W = wl.random_matrix(14, m, n, "bf16")
+    c = oracle.column_norms(W)
+    for layout in ("rowmajor", "colmajor"):
+        layer = _layer(fas, W, c, "topk", K=600, layout=layout, pass_c=False)
+        got = layer.norms().cpu().numpy()
+        ulp = np.spacing(c)
+        assert np.all(np.abs(got.astype(np.float64) - c) <= ulp), layout
+        x = wl.random_tokens(15, 1, n, "bf16")[0]
+        out = _fwd(layer, x)
+        # the library's own c differs from the oracle's in at most an ulp; compare with its own c
+        check_token(out, 0, W, got, x, "topk", K=600, ctx=f"lib-norms {layout}")
+        layer.close()
+
+
+def test_forward_is_deterministic(fas, llama_down):
+    W, c = llama_down
+    layer = _layer(fas, W, c, "topk", K=3853)
+    x = to_dev(wl.token(2, 0, 5), torch)[None, :]
+    ys = [layer.forward(x)["y"].clone() for _ in range(5)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    layer.close()
