@@ -1,0 +1,330 @@
+"""Benchmark of the weight-informed activation-sparse linear on one MI355X.
+
+Workload: the Llama-2-7B-shaped FFN down projection, W 4096 x 11008 bf16
+(std 0.02), x = SiLU(g) * u with g, u ~ N(0, 1) rounded to bf16, one token per
+step (batch-1 decode), WINA top-K at 50 % sparsity (K = 5504, the headline) and
+65 % sparsity (K = 3853). A step is one full forward: the gate kernel (scores,
+top-K select) and the product kernel (predicate, compaction, gather-GEMV).
+
+Weights rotate through 12 handle-owned copies (1.08 GB) so the 256 MB
+Infinity Cache never serves them; tokens rotate through 256 seeded tokens held
+in HBM. Steps are captured into HIP graphs and replayed, so the host's per-call
+overhead does not throttle the GPU; the timed region is bracketed by
+torch.cuda.synchronize().
+
+Printed: one JSON line with tokens/s, ms per step, the product kernel's
+achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak (its
+duration from HIP events around each launch), the same-kernel dense baseline,
+hipBLASLt's dense GEMV for context, and the CPU oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-GEMV tokens/s & achieved HBM GB/s at 50%/65% sparsity, bf16"
+PEAK_GBS = 8000.0
+RING = 12
+NTOK = 256
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3000)
+    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", choices=["sparse50", "sparse65", "dense", "all"], default="all",
+                    help="restrict the measured legs (short profiler runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for memory counters)")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(m, n, K, B=1):
+    """Bytes one product launch must move: the kept columns (K*m bf16), x and c
+    for every input (n*(2+4)), and y (m fp32)."""
+    return K * m * 2 + B * n * 2 + n * 4 + B * m * 4
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per product launch from the committed memory-counter summary,
+    or None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "product_kernel_memory_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != hashlib.sha256(open(kernel_src, "rb").read()).hexdigest():
+        return None
+    t = re.search(r"bytes per launch \(K=5504\): (\d+)", text)
+    return int(t.group(1)) if t else None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the sparse linear is measured per GPU; see DESIGN.md for how it would shard)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m, n = 4096, 11008
+    Wh = wl.weight(2, 0)
+    Wd = torch.from_numpy(Wh.view(np.int16)).to(dev).view(torch.bfloat16)
+    X = torch.from_numpy(wl.tokens(2, 0, 0, NTOK).view(np.int16)).to(dev).view(torch.bfloat16).contiguous()
+    Ks = {"sparse50": wl.k_from_sparsity(n, 0.5), "sparse65": wl.k_from_sparsity(n, 0.65)}
+    Y = torch.empty((RING, m), dtype=torch.float32, device=dev)
+
+    def make_ring(K):
+        return [fas.SparseLinear(Wd, c=None, gate="topk", K=K) for _ in range(RING)]
+
+    def layer_step(ring, dense):
+        """f(i, stream): forward of token i % 256 through ring copy i % 12."""
+        def f(i, s):
+            h, x, y = ring[i % RING], X[i % NTOK], Y[i % RING]
+            if dense:
+                fas.sparse_linear_forward_dense(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32,
+                                                s.cuda_stream)
+            else:
+                fas.sparse_linear_forward(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32, 0, 0, 0,
+                                          s.cuda_stream)
+        return f
+
+    def run_steps(f, steps, warmup):
+        """Warm up, then time exactly `steps` calls of f; returns seconds. In
+        graph mode the calls are captured in chunks of 120 and replayed."""
+        if args.mode == "eager":
+            s = torch.cuda.current_stream()
+            for i in range(warmup):
+                f(i, s)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                f(i, s)
+            torch.cuda.synchronize()
+            return time.perf_counter() - t0
+        G = RING * 10
+        cache = {}
+
+        def graph_of(count):
+            if count not in cache:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    s = torch.cuda.current_stream()
+                    for i in range(count):
+                        f(i, s)
+                cache[count] = g
+            return cache[count]
+
+        full, tail = divmod(steps, G)
+        wfull, wtail = divmod(warmup, G)
+        plan_warm = [G] * wfull + ([wtail] if wtail else [])
+        plan_timed = [G] * full + ([tail] if tail else [])
+        for cnt in set(plan_warm + plan_timed):
+            graph_of(cnt)
+        for cnt in plan_warm:
+            cache[cnt].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for cnt in plan_timed:
+            cache[cnt].replay()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    def time_graph(fn, count=600):
+        """Average microseconds per call of fn(i, stream), from HIP events on the
+        replay stream around one replay of a graph holding `count` calls
+        back to back."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            s = torch.cuda.current_stream()
+            for i in range(count):
+                fn(i, s)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / count
+
+    def kernel_times(ring, dense):
+        """(gate us, product us): each kernel launched alone, back to back. Ring
+        copy i keeps the selection of token i, so the product-only launches move
+        exactly the bytes of a full forward."""
+        if dense:
+            return 0.0, time_graph(layer_step(ring, True))
+        s0 = torch.cuda.current_stream()
+        for i in range(RING):
+            fas.sparse_linear_forward(ring[i].handle, X[i].data_ptr(), 1, Y[i].data_ptr(), fas.SL_F32,
+                                      0, 0, 0, s0.cuda_stream)
+
+        def stage(bit):
+            def f(i, s):
+                k = i % RING
+                fas.sparse_linear_forward_stages(ring[k].handle, X[k].data_ptr(), 1, Y[k].data_ptr(),
+                                                 fas.SL_F32, 0, 0, 0, bit, s.cuda_stream)
+            return f
+        gate_us = time_graph(stage(fas.SL_STAGE_GATE))
+        prod_us = time_graph(stage(fas.SL_STAGE_PRODUCT))
+        return gate_us, prod_us
+
+    results = {}
+    legs = ["sparse50", "sparse65"] if args.only == "all" else ([args.only] if args.only != "dense" else [])
+    for leg in legs:
+        K = Ks[leg]
+        ring = make_ring(K)
+        secs = run_steps(layer_step(ring, False), args.steps, args.warmup)
+        gate_us, prod_us = kernel_times(ring, False)
+        ab = algorithmic_bytes(m, n, K)
+        results[leg] = {
+            "K": K, "sparsity": 1 - K / n,
+            "tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
+            "gate_kernel_us": gate_us, "product_kernel_us": prod_us,
+            "product_algorithmic_bytes": ab,
+            "product_achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
+            "step_achieved_GBps": ab / (secs / args.steps) / 1e9,
+        }
+        for h in ring:
+            h.close()
+        del ring
+
+    dense = None
+    if args.only in ("all", "dense"):
+        ring = make_ring(Ks["sparse50"])
+        secs = run_steps(layer_step(ring, True), args.steps, args.warmup)
+        _, prod_us = kernel_times(ring, True)
+        ab = algorithmic_bytes(m, n, n)
+        dense = {"tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
+                 "product_kernel_us": prod_us, "achieved_GBps": ab / (prod_us * 1e-6) / 1e9}
+        for h in ring:
+            h.close()
+        del ring
+        # hipBLASLt / rocBLAS dense GEMV on the row-major weights, for context
+        Wr = [Wd.clone() for _ in range(RING)]
+        Yb = torch.empty((RING, m), dtype=torch.bfloat16, device=dev)
+
+        def mv(i):
+            torch.matmul(Wr[i % RING], X[i % NTOK], out=Yb[i % RING])
+        for i in range(args.warmup):
+            mv(i)
+        # hipBLASLt calls cannot be captured in a graph: time them eagerly between
+        # two events, with the GPU first asleep so the host runs ahead
+        count = 1200
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(100_000_000)
+        e0.record()
+        for i in range(count):
+            mv(i)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / count
+        dense["torch_matmul_us_per_step"] = us
+        dense["torch_matmul_tokens_per_s"] = 1e6 / us
+        del Wr
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu and "sparse50" in results:
+        cpu = cpu_baseline(wl, Wh, Ks["sparse50"], args.cpu_seconds)
+
+    head = results.get("sparse50") or results.get("sparse65")
+    out = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"] if head else None,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"] if head else None,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama2_7b_down_proj_4096x11008_bf16_topk_50pct",
+                   "m": m, "n": n, "K": Ks["sparse50"], "batch": 1, "tokens": NTOK,
+                   "weight_ring_copies": RING, "weight_ring_bytes": RING * m * n * 2,
+                   "launch": args.mode},
+    }
+    if head:
+        out["roofline"] = {
+            "bound": "hbm",
+            "achieved": round(head["product_achieved_GBps"], 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(head["product_achieved_GBps"] / PEAK_GBS, 4),
+            "traffic": traffic_from_profile(os.path.join(ROOT, "free_activation_sparse_amd", "csrc",
+                                                         "product.hip")),
+            "kernel": "product_kernel (gather-GEMV)",
+            "kernel_us": round(head["product_kernel_us"], 3),
+            "algorithmic_bytes": head["product_algorithmic_bytes"],
+        }
+    out["cpu_baseline"] = cpu
+    out["legs"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                   for k, v in results.items()}
+    if dense:
+        out["dense_same_kernel"] = {k: round(v, 4) for k, v in dense.items()}
+        for k, v in results.items():
+            bar = 0.8 / (1 - v["sparsity"])
+            out["legs"][k]["speedup_vs_dense"] = round(v["tokens_per_s"] / dense["tokens_per_s"], 4)
+            out["legs"][k]["speedup_bar"] = round(bar, 4)
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out))
+
+
+def cpu_baseline(wl, Wh, K, seconds):
+    """The oracle as it stands, per token, on the host: bounded by `seconds`."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    c = oracle.column_norms(Wh)  # init-time, not timed (the library precomputes c too)
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        x = wl.token(2, 0, done)
+        oracle.forward(Wh, c, x, "topk", K=K)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 256:
+            break
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} tokens of the 4096x11008 bf16 layer at K={K} (fp64 numpy oracle: scores, "
+                      f"lexsort top-K, gathered product), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+
+
+if __name__ == "__main__":
+    main()

@@ -22,12 +22,13 @@ SL_F32, SL_BF16 = 0, 1
 SL_W_ROWMAJOR_OUT_IN, SL_W_COLMAJOR = 0, 1
 SL_GATE_TOPK, SL_GATE_STAT, SL_GATE_FIXED = 0, 1, 2
 SL_MAX_N, SL_MAX_BATCH = 32768, 16
+SL_STAGE_GATE, SL_STAGE_PRODUCT = 1, 2
 
 EXPORTED = [
     "sparse_linear_init", "sparse_linear_forward", "sparse_linear_forward_dense",
     "sparse_linear_get_norms", "sparse_linear_destroy", "sparse_linear_strerror",
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
-    "sparse_linear_timing_enable", "sparse_linear_timing_read", "sparse_linear_set_plan",
+    "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -67,10 +68,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_last_error.restype = ctypes.c_char_p
     L.sparse_linear_normal_quantile.argtypes = [_dbl]
     L.sparse_linear_normal_quantile.restype = _dbl
-    L.sparse_linear_timing_enable.argtypes = [_vp, _i32]
-    L.sparse_linear_timing_enable.restype = ctypes.c_int
-    L.sparse_linear_timing_read.argtypes = [_vp, ctypes.POINTER(_dbl), ctypes.POINTER(_dbl), ctypes.POINTER(_i64)]
-    L.sparse_linear_timing_read.restype = ctypes.c_int
+    L.sparse_linear_forward_stages.argtypes = [_vp, _vp, _i32, _vp, ctypes.c_int, _vp, _vp, _vp, _i32, _vp]
+    L.sparse_linear_forward_stages.restype = ctypes.c_int
+    L.sparse_linear_set_deterministic.argtypes = [_vp, _i32]
+    L.sparse_linear_set_deterministic.restype = ctypes.c_int
     L.sparse_linear_set_plan.argtypes = [_vp, _i32, _i32]
     L.sparse_linear_set_plan.restype = ctypes.c_int
     _lib = L
@@ -123,15 +124,16 @@ def sparse_linear_normal_quantile(p: float) -> float:
     return lib().sparse_linear_normal_quantile(p)
 
 
-def sparse_linear_timing_enable(h: int, on: bool) -> None:
-    _check(lib().sparse_linear_timing_enable(h, 1 if on else 0), "sparse_linear_timing_enable")
+def sparse_linear_forward_stages(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, mask_ptr: int = 0,
+                                 count_ptr: int = 0, thresh_ptr: int = 0, stages: int = 3,
+                                 stream: int = 0) -> None:
+    _check(lib().sparse_linear_forward_stages(h, x_ptr, B, y_ptr, y_dtype, mask_ptr or None, count_ptr or None,
+                                              thresh_ptr or None, stages, stream or None),
+           "sparse_linear_forward_stages")
 
 
-def sparse_linear_timing_read(h: int):
-    g, p, f = _dbl(), _dbl(), _i64()
-    _check(lib().sparse_linear_timing_read(h, ctypes.byref(g), ctypes.byref(p), ctypes.byref(f)),
-           "sparse_linear_timing_read")
-    return g.value, p.value, f.value
+def sparse_linear_set_deterministic(h: int, on: bool) -> None:
+    _check(lib().sparse_linear_set_deterministic(h, 1 if on else 0), "sparse_linear_set_deterministic")
 
 
 def sparse_linear_set_plan(h: int, rows_per_tile: int, splits: int) -> None:
@@ -217,11 +219,8 @@ class SparseLinear:
     def set_plan(self, rows_per_tile: int = 0, splits: int = 0):
         sparse_linear_set_plan(self.handle, rows_per_tile, splits)
 
-    def timing(self, on: bool):
-        sparse_linear_timing_enable(self.handle, on)
-
-    def timing_read(self):
-        return sparse_linear_timing_read(self.handle)
+    def set_deterministic(self, on: bool = True):
+        sparse_linear_set_deterministic(self.handle, on)
 
     def close(self):
         if getattr(self, "handle", None):

@@ -100,8 +100,9 @@ int64_t expected_kept(const sl_linear* h, bool dense) {
   }
 }
 
-sl::Plan make_plan(const sl_linear* h, bool dense) {
+sl::Plan make_plan(const sl_linear* h, bool dense, sl_dtype ydt) {
   sl::Plan p;
+  p.atomic = (ydt == SL_F32) && !h->deterministic;
   const int vec = vec_elems(h->wdt);
   int lpc;
   if (h->plan_rows > 0) {
@@ -150,22 +151,7 @@ void free_handle(sl_linear* h) {
   (void)hipFree(h->ctr);
   (void)hipFree(h->upartials);
   (void)hipFree(h->uctr);
-  for (hipEvent_t e : h->ev) (void)hipEventDestroy(e);
   delete h;
-}
-
-sl_status record(sl_linear* h, int slot, hipStream_t s) {
-  if (!h->timing) return SL_OK;
-  const size_t need = h->ev_used + 1;
-  while (h->ev.size() < need) {
-    hipEvent_t e;
-    SL_HIP(hipEventCreate(&e));
-    h->ev.push_back(e);
-  }
-  (void)slot;
-  SL_HIP(hipEventRecord(h->ev[h->ev_used], s));
-  h->ev_used++;
-  return SL_OK;
 }
 
 }  // namespace
@@ -300,31 +286,38 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
 
 static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                               uint8_t* mask_out, int32_t* count_out, double* thresh_out, void* stream,
-                              bool dense) {
+                              bool dense, int stages) {
   g_last_error.clear();
   if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
   if (x == nullptr || y == nullptr) return fail(SL_ERR_ARG, "x and y must be non-NULL");
   if (B < 1 || B > h->max_batch) return fail(SL_ERR_ARG, "B=%d outside [1, max_batch=%d]", (int)B, h->max_batch);
   if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
+  if (stages < 1 || stages > 3) return fail(SL_ERR_ARG, "stages=%d outside 1..3", stages);
   if (B > 1) return fail(SL_ERR_UNSUPPORTED, "batched forward (B > 1) is not built yet");
   sl_status st = check_device(h);
   if (st != SL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
 
-  const bool need_gate = !dense && (h->gate != SL_GATE_FIXED || mask_out || count_out || thresh_out);
-  const sl::Plan plan = make_plan(h, dense);
-  if ((st = record(h, 0, s)) != SL_OK) return st;
-  if (need_gate) SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, s));
-  if ((st = record(h, 1, s)) != SL_OK) return st;
-  SL_HIP(sl::launch_product(h, plan, x, dense, y, y_dtype, s));
-  if ((st = record(h, 2, s)) != SL_OK) return st;
+  const sl::Plan plan = make_plan(h, dense, y_dtype);
+  // With the atomic split reduction y must start at zero: the gate kernel
+  // clears it, or a fill kernel does when no gate kernel runs. A product stage
+  // run on its own adds onto y as it stands.
+  const bool zero = plan.atomic && plan.splits > 1;
+  const bool run_gate = !dense && (stages & SL_STAGE_GATE) &&
+                        (h->gate != SL_GATE_FIXED || mask_out || count_out || thresh_out);
+  const bool full = (stages & SL_STAGE_GATE) && (stages & SL_STAGE_PRODUCT);
+  if (run_gate)
+    SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, (zero && full) ? (float*)y : nullptr, s));
+  else if (zero && full)
+    SL_HIP(sl::launch_zero((float*)y, (int64_t)B * h->m, s));
+  if (stages & SL_STAGE_PRODUCT) SL_HIP(sl::launch_product(h, plan, x, dense, y, y_dtype, s));
   return SL_OK;
 }
 
 sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                 uint8_t* mask_out, int32_t* count_out, double* thresh_out, void* stream) {
   try {
-    return forward_impl(h, x, B, y, y_dtype, mask_out, count_out, thresh_out, stream, false);
+    return forward_impl(h, x, B, y, y_dtype, mask_out, count_out, thresh_out, stream, false, 3);
   } catch (...) {
     return fail(SL_ERR_OOM, "unexpected host exception in forward");
   }
@@ -333,7 +326,7 @@ sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, 
 sl_status sparse_linear_forward_dense(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                       void* stream) {
   try {
-    return forward_impl(h, x, B, y, y_dtype, nullptr, nullptr, nullptr, stream, true);
+    return forward_impl(h, x, B, y, y_dtype, nullptr, nullptr, nullptr, stream, true, 3);
   } catch (...) {
     return fail(SL_ERR_OOM, "unexpected host exception in forward_dense");
   }
@@ -352,31 +345,19 @@ sl_status sparse_linear_destroy(sl_handle h) {
   return SL_OK;
 }
 
-sl_status sparse_linear_timing_enable(sl_handle h, int32_t on) {
-  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
-  h->timing = (on != 0);
-  h->ev_used = 0;
-  h->acc_gate_ms = h->acc_prod_ms = 0.0;
-  h->acc_fwd = 0;
-  return SL_OK;
+sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                                       uint8_t* mask_out, int32_t* count_out, double* thresh_out,
+                                       int32_t stages, void* stream) {
+  try {
+    return forward_impl(h, x, B, y, y_dtype, mask_out, count_out, thresh_out, stream, false, stages);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_stages");
+  }
 }
 
-sl_status sparse_linear_timing_read(sl_handle h, double* gate_ms, double* product_ms, int64_t* forwards) {
+sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on) {
   if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
-  double g = 0.0, p = 0.0;
-  const size_t nf = h->ev_used / 3;
-  for (size_t f = 0; f < nf; ++f) {
-    float a = 0.f, b = 0.f;
-    SL_HIP(hipEventSynchronize(h->ev[3 * f + 2]));
-    SL_HIP(hipEventElapsedTime(&a, h->ev[3 * f], h->ev[3 * f + 1]));
-    SL_HIP(hipEventElapsedTime(&b, h->ev[3 * f + 1], h->ev[3 * f + 2]));
-    g += a;
-    p += b;
-  }
-  if (gate_ms) *gate_ms = g;
-  if (product_ms) *product_ms = p;
-  if (forwards) *forwards = (int64_t)nf;
-  h->ev_used = 0;
+  h->deterministic = (on != 0);
   return SL_OK;
 }
 

@@ -31,13 +31,52 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t bal) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
 }
 
+// Cross-lane moves over DPP (data-parallel primitives): row_shr:k shifts
+// within rows of 16 lanes, row_bcast:15 / row_bcast:31 pass lane 15 of each
+// row (lane 31) on to the next row(s). Lanes whose source lies outside the
+// row keep `old`.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v, uint32_t old = 0u) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)v, CTRL, 0xf, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront (all lanes active).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t u = __shfl_up(v, d, 64);
-    if (lane >= d) v += u;
-  }
+  const uint32_t lane = threadIdx.x & 63u, rl = lane & 15u;
+  uint32_t t;
+  t = dpp_move<0x111>(v); if (rl >= 1u) v += t;   // row_shr:1
+  t = dpp_move<0x112>(v); if (rl >= 2u) v += t;   // row_shr:2
+  t = dpp_move<0x114>(v); if (rl >= 4u) v += t;   // row_shr:4
+  t = dpp_move<0x118>(v); if (rl >= 8u) v += t;   // row_shr:8
+  t = dpp_move<0x142>(v); if ((lane & 31u) >= 16u) v += t;  // row_bcast:15
+  t = dpp_move<0x143>(v); if (lane >= 32u) v += t;          // row_bcast:31
+  return v;
+}
+
+// Wavefront-uniform sum and maximum (all lanes active).
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_incl_scan(v), 63);
+}
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  const uint32_t lane = threadIdx.x & 63u, rl = lane & 15u;
+  uint32_t t;
+  t = dpp_move<0x111>(v); if (rl >= 1u) v = max(v, t);
+  t = dpp_move<0x112>(v); if (rl >= 2u) v = max(v, t);
+  t = dpp_move<0x114>(v); if (rl >= 4u) v = max(v, t);
+  t = dpp_move<0x118>(v); if (rl >= 8u) v = max(v, t);
+  t = dpp_move<0x142>(v); if ((lane & 31u) >= 16u) v = max(v, t);
+  t = dpp_move<0x143>(v); if (lane >= 32u) v = max(v, t);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Sum over each aligned group of 16 lanes, valid in the group's last lane.
+__device__ __forceinline__ uint32_t row16_sum_in_last(uint32_t v) {
+  const uint32_t rl = threadIdx.x & 15u;
+  uint32_t t;
+  t = dpp_move<0x111>(v); if (rl >= 1u) v += t;
+  t = dpp_move<0x112>(v); if (rl >= 2u) v += t;
+  t = dpp_move<0x114>(v); if (rl >= 4u) v += t;
+  t = dpp_move<0x118>(v); if (rl >= 8u) v += t;
   return v;
 }
 

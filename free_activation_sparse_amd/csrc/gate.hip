@@ -3,17 +3,27 @@
 // set and publishes it as a threshold pair (kthr, jlast); the product kernels
 // re-evaluate the same predicate on their own input chunks.
 //
-//  * Top-K (WINA article, section 一): radix select of the K-th largest score
-//    on its fp32 bit pattern, digits of 12, 12 and 7 bits with LDS histograms,
-//    then the rank of the last kept tie in index order by wavefront ballots.
+//  * Top-K (WINA article, section 一): selection on the scores' fp32 bit
+//    patterns (non-negative, so unsigned order is numeric order).
+//    Fast path: a 4096-bin LDS histogram of key>>14 over the eight binades
+//    below the largest key (512 bins per binade: few atomic collisions); the
+//    pivot bin's keys (at most 64) are compacted with ballots and ranked
+//    exactly under the order (score descending, index ascending).
+//    General path (pivot below the window, or more than 64 keys in the pivot
+//    bin, i.e. heavy ties): radix select on 12/12/7-bit key digits, then the
+//    kept ties' last index by a radix select on the index (8/7 bits).
 //  * Statistical threshold (Spark Transformer article, section 2.2): mean and
 //    population variance of the scores in double-double arithmetic, each
 //    rounded once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)).
 //  * Fixed threshold: kthr from the per-layer tau (WINA article, section 三,
 //    calibrated per-layer thresholds).
 //
-// Element i of the token is held by thread (i mod 1024) in register slot
-// (i / 1024), so every global load is one coalesced row of the token.
+// Layout: elements come in groups of 4 consecutive inputs; thread t holds
+// groups t, t + 1024, ... (G groups), loaded with vector loads (8 bytes of
+// bf16 or 16 bytes of fp32 x, 16 bytes of c) when n is a multiple of 4 and x
+// is aligned to its vector, else with scalar loads.
+// Every load is unconditional (index clamped, value masked), so all of a
+// thread's loads are in flight together.
 #include "device_common.h"
 #include "internal.h"
 
@@ -34,12 +44,25 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) 
   if (lane == 63) wsum[w] = inc;
   __syncthreads();
   uint32_t off = 0;
-  for (int k = 0; k < w; ++k) off += wsum[k];
+#pragma unroll
+  for (int k = 0; k < GW; ++k) off += (k < w) ? wsum[k] : 0u;
   return inc + off;
 }
 
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  v = wave_sum(v);
+  if (lane == 0) wsum[w] = v;
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < GW; ++k) tot += wsum[k];
+  return tot;
+}
+
 // Find bin b of an NB-bin histogram such that (count of bins above b) < r <=
-// (count of bins above b) + hist[b]. Writes res[0] = b, res[1] = count above.
+// (count of bins above b) + hist[b]. Writes res[0] = b, res[1] = count above;
+// leaves res untouched when the histogram holds fewer than r entries.
 template <int NB>
 __device__ void find_bin(const uint32_t* hist, uint32_t r, uint32_t* wsum, uint32_t* res) {
   constexpr int BPT = (NB + GT - 1) / GT;
@@ -119,41 +142,68 @@ __device__ __forceinline__ void thresh_to_key(double t, int n, uint32_t& kthr, i
   }
 }
 
-template <typename XT, int E, int MODE>
-__global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, const float* __restrict__ c,
-                                                  int n, int K, double z, float tau,
-                                                  sl::GateOut* __restrict__ gout,
-                                                  uint8_t* __restrict__ mask_out,
-                                                  int32_t* __restrict__ count_out,
-                                                  double* __restrict__ thresh_out) {
-  __shared__ uint32_t h1[MODE == MODE_TOPK ? 4096 : 1];
-  __shared__ uint32_t h2[MODE == MODE_TOPK ? 4096 : 1];
-  __shared__ uint32_t h3[MODE == MODE_TOPK ? 128 : 1];
-  __shared__ uint32_t table[MODE == MODE_TOPK ? E * GW : 1];
-  __shared__ uint32_t wsum[GW];
-  __shared__ uint32_t res[4];
-  __shared__ dd dsum[GW][2];
-  __shared__ uint32_t kminmax[GW][2];
-  __shared__ uint32_t s_kthr;
-  __shared__ int s_jlast;
+// ---------------------------------------------------------------- loads
+// Keys of group g (4 inputs starting at 4 * (g * GT + t)); out-of-range
+// inputs get key 0 and must be masked by the caller with their index.
+template <typename XT, bool VEC>
+__device__ __forceinline__ void load_group(const XT* __restrict__ xb, const float* __restrict__ c, int n, int g,
+                                           uint32_t (&k)[4]) {
+  const int base = (g * GT + (int)threadIdx.x) * 4;
+  float xv[4], cv[4];
+  if constexpr (VEC) {
+    const int bc = base < n ? base : 0;  // n % 4 == 0: groups are all-in or all-out
+    if constexpr (sizeof(XT) == 2) {
+      const uint2 v = *(const uint2*)(xb + bc);
+      xv[0] = __uint_as_float(v.x << 16);
+      xv[1] = __uint_as_float(v.x & 0xffff0000u);
+      xv[2] = __uint_as_float(v.y << 16);
+      xv[3] = __uint_as_float(v.y & 0xffff0000u);
+    } else {
+      const float4 a = *(const float4*)(xb + bc);
+      xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w;
+    }
+    const float4 a = *(const float4*)(c + bc);
+    cv[0] = a.x; cv[1] = a.y; cv[2] = a.z; cv[3] = a.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = base + e;
+      const int ic = i < n ? i : n - 1;
+      xv[e] = load_elem(xb + ic);
+      cv[e] = c[ic];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) k[e] = (base + e < n) ? score_key(xv[e], cv[e]) : 0u;
+}
 
+template <typename XT, int G, int MODE, bool VEC>
+__device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float* __restrict__ c, int n, int K,
+                                          double z, float tau, sl::GateOut* __restrict__ gout,
+                                          uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
+                                          double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
+                                          uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
+                                          uint32_t* res, uint64_t* cand, dd (*dsum)[2],
+                                          uint32_t (*kminmax)[2]) {
+  constexpr int E = 4 * G;
   const int b = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const XT* xb = x + (size_t)b * n;
-
-  if constexpr (MODE == MODE_TOPK) {
-    for (int i = t; i < 4096; i += GT) {
-      h1[i] = 0u;
-      h2[i] = 0u;
-    }
-    if (t < 128) h3[t] = 0u;
-  }
+  auto index = [&](int e) { return ((e >> 2) * GT + t) * 4 + (e & 3); };
 
   uint32_t key[E];
 #pragma unroll
-  for (int r = 0; r < E; ++r) {
-    const int i = r * GT + t;
-    key[r] = (i < n) ? score_key(load_elem(xb + i), c[i]) : 0u;
+  for (int g = 0; g < G; ++g) {
+    uint32_t k4[4];
+    load_group<XT, VEC>(xb, c, n, g, k4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) key[g * 4 + e] = k4[e];
+  }
+
+  // the product kernel that follows adds its split partials into y atomically
+  if (zero_y != nullptr) {
+    float* yb = zero_y + (size_t)b * m;
+    for (int i = t; i < m; i += GT) yb[i] = 0.f;
   }
 
   uint32_t kthr = 0xffffffffu;
@@ -166,71 +216,120 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
     if (K == 0) {
       thresh = __longlong_as_double(0x7ff0000000000000ll);  // +inf: nothing kept
     } else {
-      __syncthreads();  // histograms cleared
-      // pass 1: bits 30..19
+      for (int i = t; i < 4096; i += GT) h1[i] = 0u;
+      uint32_t lmax = 0u;
 #pragma unroll
-      for (int r = 0; r < E; ++r)
-        if (r * GT + t < n) atomicAdd(&h1[key[r] >> 19], 1u);
+      for (int e = 0; e < E; ++e) lmax = max(lmax, key[e]);  // padding keys are 0
+      lmax = wave_max(lmax);
+      if (lane == 0) wsum[w] = lmax;
+      if (t == 0) {
+        res[0] = 0xffffffffu;  // "not found" unless find_bin writes it
+        res[3] = 0u;           // candidate counter
+      }
+      __syncthreads();  // h1 cleared, maxima and res published
+      uint32_t kmax = wsum[0];
+#pragma unroll
+      for (int k = 1; k < GW; ++k) kmax = max(kmax, wsum[k]);
+      const uint32_t top = kmax >> 14;
+      const uint32_t base = top >= 4095u ? top - 4095u : 0u;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint32_t d = (key[e] >> 14) - base;  // wraps above 4095 when below the window
+        if (d < 4096u && index(e) < n) atomicAdd(&h1[d], 1u);
+      }
       __syncthreads();
       find_bin<4096>(h1, (uint32_t)K, wsum, res);
-      const uint32_t b1 = res[0];
-      uint32_t rr = (uint32_t)K - res[1];
-      // pass 2: bits 18..7 among keys whose bits 30..19 equal b1
+      const bool in_window = res[0] != 0xffffffffu;
+      const uint32_t c1 = in_window ? h1[res[0]] : 0u;
+      if (in_window && c1 <= 64u) {
+        const uint32_t b1 = res[0] + base;
+        const uint32_t r1 = (uint32_t)K - res[1];  // rank wanted inside the pivot bin, 1-based
+        // candidates as (key, ~index): larger composite = earlier in the order
+        // (score descending, index ascending); composites are distinct
 #pragma unroll
-      for (int r = 0; r < E; ++r)
-        if (r * GT + t < n && (key[r] >> 19) == b1) atomicAdd(&h2[(key[r] >> 7) & 0xfffu], 1u);
-      __syncthreads();
-      find_bin<4096>(h2, rr, wsum, res);
-      const uint32_t p2 = (b1 << 12) | res[0];
-      rr -= res[1];
-      // pass 3: bits 6..0
-#pragma unroll
-      for (int r = 0; r < E; ++r)
-        if (r * GT + t < n && (key[r] >> 7) == p2) atomicAdd(&h3[key[r] & 0x7fu], 1u);
-      __syncthreads();
-      find_bin<128>(h3, rr, wsum, res);
-      const uint32_t vstar = (p2 << 7) | res[0];
-      const uint32_t need = rr - res[1];  // ties at vstar to keep, lowest index first (>= 1)
-
-      // rank of each tie in index order: per-(slot, wavefront) counts, scanned
-#pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const bool p = (r * GT + t < n) && key[r] == vstar;
-        const uint64_t bal = __ballot(p);
-        if (lane == 0) table[r * GW + w] = (uint32_t)__popcll(bal);
-      }
-      __syncthreads();
-      if (w == 0) {
-        constexpr int NT = E * GW;
-        constexpr int PER = (NT + 63) / 64;
-        uint32_t v[PER];
-        uint32_t s = 0;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int idx = lane * PER + q;
-          v[q] = idx < NT ? table[idx] : 0u;
-          s += v[q];
+        for (int e = 0; e < E; ++e) {
+          const int i = index(e);
+          const bool p = i < n && (key[e] >> 14) == b1;
+          const uint64_t bal = __ballot(p);
+          if (bal != 0ull) {
+            uint32_t off = 0u;
+            if (lane == 0) off = atomicAdd(&res[3], (uint32_t)__popcll(bal));
+            off = (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
+            if (p) cand[off + lanes_below(bal)] = ((uint64_t)key[e] << 32) | (uint64_t)(~(uint32_t)i);
+          }
         }
-        uint32_t run = wave_incl_scan(s) - s;
+        __syncthreads();
+        // rank of candidate a among the c1: 16 threads per candidate, 4 each
+        const uint32_t a = (uint32_t)t >> 4, part = (uint32_t)t & 15u;
+        const uint64_t ca = a < c1 ? cand[a] : 0ull;
+        uint32_t above = 0u;
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-          const int idx = lane * PER + q;
-          if (idx < NT) table[idx] = run;
-          run += v[q];
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t u = part * 4u + (uint32_t)q;
+          above += (u < c1 && cand[u] > ca) ? 1u : 0u;
         }
-      }
-      __syncthreads();
+        above = row16_sum_in_last(above);
+        if (part == 15u && a < c1 && above == r1 - 1u) {
+          res[1] = (uint32_t)(ca >> 32);
+          res[2] = ~(uint32_t)ca;
+        }
+        __syncthreads();
+        kthr = res[1];
+        jlast = (int)res[2];
+      } else {
+        // ---- general path: radix select on key digits 30..19, 18..7, 6..0
+        for (int i = t; i < 4096; i += GT) {
+          h1[i] = 0u;
+          h2[i] = 0u;
+        }
+        if (t < 128) h3[t] = 0u;
+        __syncthreads();
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const int i = r * GT + t;
-        const bool p = (i < n) && key[r] == vstar;
-        const uint64_t bal = __ballot(p);
-        if (p && table[r * GW + w] + lanes_below(bal) == need - 1u) res[2] = (uint32_t)i;
+        for (int e = 0; e < E; ++e)
+          if (index(e) < n) atomicAdd(&h1[key[e] >> 19], 1u);
+        __syncthreads();
+        find_bin<4096>(h1, (uint32_t)K, wsum, res);
+        const uint32_t b1 = res[0];
+        uint32_t rr = (uint32_t)K - res[1];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (index(e) < n && (key[e] >> 19) == b1) atomicAdd(&h2[(key[e] >> 7) & 0xfffu], 1u);
+        __syncthreads();
+        find_bin<4096>(h2, rr, wsum, res);
+        const uint32_t p2 = (b1 << 12) | res[0];
+        rr -= res[1];
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (index(e) < n && (key[e] >> 7) == p2) atomicAdd(&h3[key[e] & 0x7fu], 1u);
+        __syncthreads();
+        find_bin<128>(h3, rr, wsum, res);
+        const uint32_t vstar = (p2 << 7) | res[0];
+        const uint32_t need = rr - res[1];  // ties at vstar to keep, lowest index first (>= 1)
+        // the need-th smallest index among keys equal to vstar: bins are
+        // stored reversed so that find_bin's descending search runs upwards
+        if (t < 256) h2[t] = 0u;
+        if (t < 128) h3[t] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = index(e);
+          if (i < n && key[e] == vstar) atomicAdd(&h2[255 - (i >> 7)], 1u);
+        }
+        __syncthreads();
+        find_bin<256>(h2, need, wsum, res);
+        const uint32_t hiidx = 255u - res[0];
+        const uint32_t need2 = need - res[1];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = index(e);
+          if (i < n && key[e] == vstar && (uint32_t)(i >> 7) == hiidx) atomicAdd(&h3[127 - (i & 127)], 1u);
+        }
+        __syncthreads();
+        find_bin<128>(h3, need2, wsum, res);
+        kthr = vstar;
+        jlast = (int)((hiidx << 7) | (127u - res[0]));
       }
-      __syncthreads();
-      kthr = vstar;
-      jlast = (int)res[2];
-      thresh = (double)__uint_as_float(vstar);
+      thresh = (double)__uint_as_float(kthr);
     }
   } else {
     if constexpr (MODE == MODE_STAT) {
@@ -238,17 +337,17 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
       double a1 = 0.0, e1 = 0.0, a2 = 0.0, e2 = 0.0;
       uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        if (r * GT + t < n) {
-          const double s = (double)__uint_as_float(key[r]);
+      for (int e = 0; e < E; ++e) {
+        if (index(e) < n) {
+          const double s = (double)__uint_as_float(key[e]);
           dd p = two_sum(a1, s);
           a1 = p.hi;
           e1 = e1 + p.lo;
           p = two_sum(a2, s * s);
           a2 = p.hi;
           e2 = e2 + p.lo;
-          kmin = min(kmin, key[r]);
-          kmax = max(kmax, key[r]);
+          kmin = min(kmin, key[e]);
+          kmax = max(kmax, key[e]);
         }
       }
       dd S1 = fast_two_sum(a1, e1), S2 = fast_two_sum(a2, e2);
@@ -256,9 +355,9 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
       for (int d = 32; d >= 1; d >>= 1) {
         S1 = dd_add(S1, shfl_xor_dd(S1, d));
         S2 = dd_add(S2, shfl_xor_dd(S2, d));
-        kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
-        kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
       }
+      kmax = wave_max(kmax);
+      kmin = ~wave_max(~kmin);
       if (lane == 0) {
         dsum[w][0] = S1;
         dsum[w][1] = S2;
@@ -293,13 +392,13 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
         uint32_t kt;
         int jl;
         thresh_to_key(tt, n, kt, jl);
-        s_kthr = kt;
-        s_jlast = jl;
+        res[0] = kt;
+        res[1] = (uint32_t)jl;
         dsum[0][0].hi = tt;
       }
       __syncthreads();
-      kthr = s_kthr;
-      jlast = s_jlast;
+      kthr = res[0];
+      jlast = (int)res[1];
       thresh = dsum[0][0].hi;
     } else {  // MODE_FIXED
       thresh = (double)tau;
@@ -308,73 +407,93 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
     if (count_out != nullptr) {
       uint32_t local = 0;
 #pragma unroll
-      for (int r = 0; r < E; ++r) {
-        const int i = r * GT + t;
-        local += (i < n && gate_keep(key[r], i, kthr, jlast)) ? 1u : 0u;
+      for (int e = 0; e < E; ++e) {
+        const int i = index(e);
+        local += (i < n && gate_keep(key[e], i, kthr, jlast)) ? 1u : 0u;
       }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) local += (uint32_t)__shfl_xor((int)local, d, 64);
-      if (lane == 0) wsum[w] = local;
-      __syncthreads();
-      uint32_t tot = 0;
-      for (int k = 0; k < GW; ++k) tot += wsum[k];
-      count = (int)tot;
+      count = (int)block_sum(local, wsum);
     }
   }
 
   if (mask_out != nullptr) {
     uint8_t* mb = mask_out + (size_t)b * n;
 #pragma unroll
-    for (int r = 0; r < E; ++r) {
-      const int i = r * GT + t;
-      if (i < n) mb[i] = gate_keep(key[r], i, kthr, jlast) ? 1 : 0;
+    for (int e = 0; e < E; ++e) {
+      const int i = index(e);
+      if (i < n) mb[i] = gate_keep(key[e], i, kthr, jlast) ? 1 : 0;
     }
   }
   if (t == 0) {
-    sl::GateOut g;
-    g.kthr = kthr;
-    g.jlast = jlast;
-    g.count = count;
-    g.pad = 0;
-    g.thresh = thresh;
-    gout[b] = g;
+    sl::GateOut go;
+    go.kthr = kthr;
+    go.jlast = jlast;
+    go.count = count;
+    go.pad = 0;
+    go.thresh = thresh;
+    gout[b] = go;
     if (count_out != nullptr) count_out[b] = count;
     if (thresh_out != nullptr) thresh_out[b] = thresh;
   }
 }
 
-template <typename XT, int E>
-hipError_t launch_e(const sl_linear* h, const void* x, int B, uint8_t* mask, int32_t* cnt, double* th,
+template <typename XT, int G, int MODE>
+__global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, const float* __restrict__ c, int n,
+                                                  int K, double z, float tau, sl::GateOut* __restrict__ gout,
+                                                  uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
+                                                  double* __restrict__ thresh_out, float* __restrict__ zero_y,
+                                                  int m, int vec) {
+  __shared__ uint32_t h1[MODE == MODE_TOPK ? 4096 : 1];
+  __shared__ uint32_t h2[MODE == MODE_TOPK ? 4096 : 1];
+  __shared__ uint32_t h3[MODE == MODE_TOPK ? 128 : 1];
+  __shared__ uint64_t cand[MODE == MODE_TOPK ? 64 : 1];
+  __shared__ uint32_t wsum[GW];
+  __shared__ uint32_t res[4];
+  __shared__ dd dsum[MODE == MODE_STAT ? GW : 1][2];
+  __shared__ uint32_t kminmax[MODE == MODE_STAT ? GW : 1][2];
+  if (vec)
+    gate_body<XT, G, MODE, true>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2, h3,
+                                 wsum, res, cand, dsum, kminmax);
+  else
+    gate_body<XT, G, MODE, false>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2,
+                                  h3, wsum, res, cand, dsum, kminmax);
+}
+
+template <typename XT, int G>
+hipError_t launch_g(const sl_linear* h, const void* x, int B, uint8_t* mask, int32_t* cnt, double* th, float* zy,
                     hipStream_t s) {
   const XT* xp = (const XT*)x;
   const int n = (int)h->n;
+  const int vec = (n % 4 == 0 && ((uintptr_t)x % (4 * sizeof(XT))) == 0) ? 1 : 0;
   switch (h->gate) {
     case SL_GATE_TOPK:
-      gate_kernel<XT, E, MODE_TOPK><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt, th);
+      gate_kernel<XT, G, MODE_TOPK><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt, th,
+                                                     zy, (int)h->m, vec);
       break;
     case SL_GATE_STAT:
-      gate_kernel<XT, E, MODE_STAT><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt, th);
+      gate_kernel<XT, G, MODE_STAT><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt, th,
+                                                     zy, (int)h->m, vec);
       break;
     default:
-      gate_kernel<XT, E, MODE_FIXED><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt, th);
+      gate_kernel<XT, G, MODE_FIXED><<<B, GT, 0, s>>>(xp, h->c, n, (int)h->K, h->z, h->tau, h->gout, mask, cnt,
+                                                      th, zy, (int)h->m, vec);
       break;
   }
   return hipGetLastError();
 }
 
 template <typename XT>
-hipError_t launch_t(const sl_linear* h, const void* x, int B, uint8_t* mask, int32_t* cnt, double* th,
+hipError_t launch_t(const sl_linear* h, const void* x, int B, uint8_t* mask, int32_t* cnt, double* th, float* zy,
                     hipStream_t s) {
-  const int e = (int)((h->n + GT - 1) / GT);
-  if (e <= 1) return launch_e<XT, 1>(h, x, B, mask, cnt, th, s);
-  if (e <= 2) return launch_e<XT, 2>(h, x, B, mask, cnt, th, s);
-  if (e <= 4) return launch_e<XT, 4>(h, x, B, mask, cnt, th, s);
-  if (e <= 8) return launch_e<XT, 8>(h, x, B, mask, cnt, th, s);
-  if (e <= 12) return launch_e<XT, 12>(h, x, B, mask, cnt, th, s);
-  if (e <= 16) return launch_e<XT, 16>(h, x, B, mask, cnt, th, s);
-  if (e <= 20) return launch_e<XT, 20>(h, x, B, mask, cnt, th, s);
-  if (e <= 24) return launch_e<XT, 24>(h, x, B, mask, cnt, th, s);
-  return launch_e<XT, 32>(h, x, B, mask, cnt, th, s);
+  const int groups = (int)((h->n + 4 * GT - 1) / (4 * GT));  // 1..8 for n <= 32768
+  switch (groups) {
+    case 1: return launch_g<XT, 1>(h, x, B, mask, cnt, th, zy, s);
+    case 2: return launch_g<XT, 2>(h, x, B, mask, cnt, th, zy, s);
+    case 3: return launch_g<XT, 3>(h, x, B, mask, cnt, th, zy, s);
+    case 4: return launch_g<XT, 4>(h, x, B, mask, cnt, th, zy, s);
+    case 5: return launch_g<XT, 5>(h, x, B, mask, cnt, th, zy, s);
+    case 6: return launch_g<XT, 6>(h, x, B, mask, cnt, th, zy, s);
+    default: return launch_g<XT, 8>(h, x, B, mask, cnt, th, zy, s);
+  }
 }
 
 }  // namespace
@@ -382,9 +501,9 @@ hipError_t launch_t(const sl_linear* h, const void* x, int B, uint8_t* mask, int
 namespace sl {
 
 hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_out, int32_t* count_out,
-                       double* thresh_out, hipStream_t s) {
-  if (h->wdt == SL_BF16) return launch_t<uint16_t>(h, x, B, mask_out, count_out, thresh_out, s);
-  return launch_t<float>(h, x, B, mask_out, count_out, thresh_out, s);
+                       double* thresh_out, float* zero_y, hipStream_t s) {
+  if (h->wdt == SL_BF16) return launch_t<uint16_t>(h, x, B, mask_out, count_out, thresh_out, zero_y, s);
+  return launch_t<float>(h, x, B, mask_out, count_out, thresh_out, zero_y, s);
 }
 
 }  // namespace sl

@@ -7,7 +7,7 @@
 
 #include <vector>
 
-#include "../../include/sparse_linear.h"
+#include "sparse_linear.h"
 
 namespace sl {
 
@@ -38,6 +38,7 @@ struct Plan {
   int splits;  // input chunks
   int chunk;   // inputs per chunk
   int unroll;  // columns in flight per lane group
+  bool atomic; // fp32 atomic split reduction into y (else ordered, reproducible)
 };
 
 // Matrix-core (union) product plan.
@@ -71,12 +72,8 @@ struct sl_linear {
   uint32_t* uctr = nullptr;     // [utiles]
 
   int plan_rows = 0, plan_splits = 0;  // overrides (0 = automatic)
+  bool deterministic = false;          // ordered split reduction for fp32 y too
 
-  bool timing = false;
-  std::vector<hipEvent_t> ev;   // 3 per forward: start, after gate, after product
-  size_t ev_used = 0;
-  double acc_gate_ms = 0.0, acc_prod_ms = 0.0;
-  int64_t acc_fwd = 0;
 };
 
 namespace sl {
@@ -85,7 +82,8 @@ namespace sl {
 hipError_t launch_repack(const void* W, sl_dtype dt, int64_t m, int64_t n, void* Wt, hipStream_t s);
 hipError_t launch_norms(const void* Wt, sl_dtype dt, int64_t m, int64_t n, float* c, hipStream_t s);
 hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_out,
-                       int32_t* count_out, double* thresh_out, hipStream_t s);
+                       int32_t* count_out, double* thresh_out, float* zero_y, hipStream_t s);
+hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, bool dense, void* y,
                           sl_dtype ydt, hipStream_t s);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,

@@ -147,15 +147,29 @@ const char* sparse_linear_last_error(void);
 double sparse_linear_normal_quantile(double p);
 
 /*
- * Kernel timing for measurement. When enabled (on != 0), each forward records
- * HIP events around its gate kernel and its product kernel on the forward's
- * stream; sparse_linear_timing_read() synchronizes on the recorded events and
- * returns the summed durations in milliseconds and the number of forwards
- * recorded since the last read (then resets). Off by default.
+ * sparse_linear_forward_stages -- run part of a forward, for measurement.
+ * stages is a bit mask: SL_STAGE_GATE (scores and selection, writes the
+ * optional outputs) and SL_STAGE_PRODUCT (the gathered product, using the
+ * selection the handle's most recent gate stage left for those B tokens).
+ * stages == SL_STAGE_GATE | SL_STAGE_PRODUCT is exactly sparse_linear_forward.
+ * Running the product stage alone repeats the previous selection's product;
+ * it lets a caller time each kernel on its own. Other arguments as for
+ * sparse_linear_forward; stages outside 1..3 give SL_ERR_ARG.
  */
-sl_status sparse_linear_timing_enable(sl_handle h, int32_t on);
-sl_status sparse_linear_timing_read(sl_handle h, double* gate_ms, double* product_ms,
-                                    int64_t* forwards);
+#define SL_STAGE_GATE 1
+#define SL_STAGE_PRODUCT 2
+sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
+                                       uint8_t* mask_out, int32_t* count_out, double* thresh_out,
+                                       int32_t stages, void* stream);
+
+/*
+ * Split reduction mode. The product kernel splits the kept inputs into chunks
+ * whose partial sums are added per output row. By default (on == 0) fp32
+ * outputs take fp32 atomic adds, which is fastest but lets the summation order
+ * vary between runs in the last bits. With on != 0 the partials are added in a
+ * fixed order (bit-reproducible runs). bf16 outputs always use the fixed order.
+ */
+sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on);
 
 /*
  * Launch-shape override for tuning sweeps: rows_per_tile in {128, 256, 512}

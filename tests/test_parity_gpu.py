@@ -196,6 +196,7 @@ def test_topk_all_equals_dense_kernel(fas):
     W = wl.random_matrix(10, m, n, "bf16")
     c = oracle.column_norms(W)
     layer = _layer(fas, W, c, "topk", K=n)
+    layer.set_deterministic(True)  # ordered reduction: same kernel, same bits
     x = to_dev(wl.random_tokens(11, 1, n, "bf16")[0], torch)[None, :]
     ys = layer.forward(x)["y"]
     yd = layer.forward_dense(x)
@@ -259,11 +260,83 @@ def test_library_norms_and_colmajor_layout(fas):
 
 
 def test_forward_is_deterministic(fas, llama_down):
+    """With the ordered split reduction repeated forwards agree to the bit; the
+    default atomic reduction agrees to fp32 summation-order rounding."""
     W, c = llama_down
     layer = _layer(fas, W, c, "topk", K=3853)
     x = to_dev(wl.token(2, 0, 5), torch)[None, :]
+    ya = [layer.forward(x)["y"].clone() for _ in range(5)]
+    layer.set_deterministic(True)
     ys = [layer.forward(x)["y"].clone() for _ in range(5)]
+    ys.append(layer.forward(x, y_dtype=torch.bfloat16)["y"].float())
     torch.cuda.synchronize()
-    for y in ys[1:]:
+    for y in ys[1:5]:
         assert torch.equal(y, ys[0])
+    for y in ya:
+        assert rel_l2(y.cpu().numpy(), ys[0].cpu().numpy()) <= 1e-6
+    assert rel_l2(ys[5].cpu().numpy(), ys[0].cpu().numpy()) <= 4e-3
+    layer.close()
+
+
+def test_graph_replay_matches_eager(fas, llama_down):
+    """Forwards captured in a HIP graph give the eager results on every replay,
+    with eager work and synchronizations between the replays."""
+    W, c = llama_down
+    m = W.shape[0]
+    layers = [_layer(fas, W, c, "topk", K=3853), _layer(fas, W, c, "topk", K=5504)]
+    for l in layers:
+        l.set_deterministic(True)
+    xs = [to_dev(wl.token(2, 0, t), torch)[None, :] for t in range(6)]
+    eager = [layers[i % 2].forward(x)["y"].clone() for i, x in enumerate(xs)]
+    torch.cuda.synchronize()
+    ys = [torch.empty((1, m), dtype=torch.float32, device="cuda:0") for _ in xs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i, (x, y) in enumerate(zip(xs, ys)):
+            layers[i % 2].forward(x, y=y)
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        layers[0].forward(xs[rep])  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (y, e) in enumerate(zip(ys, eager)):
+            assert torch.equal(y, e), f"replay {rep} forward {i}"
+    for l in layers:
+        l.close()
+
+
+@pytest.mark.parametrize("det", [False, True])
+def test_reduction_modes_match_oracle(fas, llama_down, det):
+    """Both split reductions (atomic fp32, ordered) and the bf16 output, at
+    several launch shapes, on the full Llama-7B down projection."""
+    W, c = llama_down
+    K = wl.k_from_sparsity(W.shape[1], 0.5)
+    layer = _layer(fas, W, c, "topk", K=K)
+    layer.set_deterministic(det)
+    rows = np.arange(0, W.shape[0], 41)
+    for rpt, splits in ((128, 16), (256, 32), (512, 0), (128, 1)):
+        layer.set_plan(rpt, splits)
+        for t in range(2):
+            x = wl.token(2, 0, 40 + t)
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=rows, ctx=f"det={det} {rpt}/{splits}")
+            check_token(_fwd(layer, x, y_dtype=torch.bfloat16), 0, W, c, x, "topk", K=K, rows=rows,
+                        ctx=f"det={det} bf16 {rpt}/{splits}")
+    layer.close()
+
+
+def test_dense_forward_modes(fas, llama_down):
+    W, c = llama_down
+    layer = _layer(fas, W, c, "topk", K=10)
+    x = wl.token(2, 0, 7)
+    xd = to_dev(x, torch)[None, :]
+    ref = oracle.sparse_product(W, x, np.arange(W.shape[1]))
+    for det in (False, True):
+        layer.set_deterministic(det)
+        y = layer.forward_dense(xd)
+        yb = layer.forward_dense(xd, y_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert rel_l2(y[0].cpu().numpy(), ref) <= REL_L2_TOL
+        assert rel_l2(yb[0].float().cpu().numpy(), ref) <= REL_L2_TOL
     layer.close()
