@@ -135,6 +135,23 @@ sl::Plan make_plan(const sl_linear* h, bool dense, sl_dtype ydt) {
   return p;
 }
 
+// Union (B > 1) product: 128-row tiles; input chunks of 256..512 so that about
+// 1536 workgroups are in flight.
+int max_union_splits(int64_t n) { return (int)std::max<int64_t>(1, (n + sl::kUnionMinChunk - 1) / sl::kUnionMinChunk); }
+
+sl::UnionPlan make_union_plan(const sl_linear* h, sl_dtype ydt) {
+  sl::UnionPlan p;
+  p.atomic = (ydt == SL_F32) && !h->deterministic;
+  p.tiles = (int)((h->m + 127) / 128);
+  const int64_t n = h->n;
+  int splits = (int)std::max<int64_t>(1, 1536 / p.tiles);
+  splits = std::min(splits, max_union_splits(n));
+  splits = std::max<int>(splits, (int)((n + sl::kUnionMaxChunk - 1) / sl::kUnionMaxChunk));
+  p.chunk = (int)((n + splits - 1) / splits);
+  p.splits = (int)((n + p.chunk - 1) / p.chunk);
+  return p;
+}
+
 sl_status check_device(const sl_linear* h) {
   int dev = -1;
   SL_HIP(hipGetDevice(&dev));
@@ -243,6 +260,16 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
     if ((e = hipMemsetAsync(h->ctr, 0, (size_t)h->ctr_len * sizeof(uint32_t), s)) != hipSuccess)
       return cleanup_fail(e, "hipMemsetAsync(counters)");
 
+    if (max_batch > 1 && w_dtype == SL_BF16) {
+      h->upart_len = (int64_t)max_union_splits(n) * max_batch * m;
+      if ((e = hipMalloc(&h->upartials, (size_t)h->upart_len * sizeof(float))) != hipSuccess)
+        return cleanup_fail(e, "hipMalloc(union partials)");
+      const size_t uc = (size_t)((m + 127) / 128);
+      if ((e = hipMalloc(&h->uctr, uc * sizeof(uint32_t))) != hipSuccess)
+        return cleanup_fail(e, "hipMalloc(union counters)");
+      if ((e = hipMemsetAsync(h->uctr, 0, uc * sizeof(uint32_t), s)) != hipSuccess)
+        return cleanup_fail(e, "hipMemsetAsync(union counters)");
+    }
     if (w_layout == SL_W_ROWMAJOR_OUT_IN) {
       if ((e = sl::launch_repack(W, w_dtype, m, n, h->Wt, s)) != hipSuccess) return cleanup_fail(e, "repack");
     } else {
@@ -293,24 +320,43 @@ static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl
   if (B < 1 || B > h->max_batch) return fail(SL_ERR_ARG, "B=%d outside [1, max_batch=%d]", (int)B, h->max_batch);
   if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
   if (stages < 1 || stages > 3) return fail(SL_ERR_ARG, "stages=%d outside 1..3", stages);
-  if (B > 1) return fail(SL_ERR_UNSUPPORTED, "batched forward (B > 1) is not built yet");
   sl_status st = check_device(h);
   if (st != SL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
+  const bool full = (stages & SL_STAGE_GATE) && (stages & SL_STAGE_PRODUCT);
+  const bool gate_wanted = !dense && (stages & SL_STAGE_GATE) &&
+                           (h->gate != SL_GATE_FIXED || mask_out || count_out || thresh_out);
+  const size_t ysz = (y_dtype == SL_BF16) ? 2 : 4;
 
+  if (B > 1 && h->wdt == SL_BF16) {
+    // one matrix-core pass over the union of the B kept sets
+    const sl::UnionPlan up = make_union_plan(h, y_dtype);
+    const bool zero = up.atomic && up.splits > 1;
+    if (gate_wanted)
+      SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, (zero && full) ? (float*)y : nullptr, s));
+    else if (zero && full)
+      SL_HIP(sl::launch_zero((float*)y, (int64_t)B * h->m, s));
+    if (stages & SL_STAGE_PRODUCT) SL_HIP(sl::launch_union_product(h, up, x, B, dense, y, y_dtype, s));
+    return SL_OK;
+  }
+
+  // one token at a time through the single-token product kernel (B == 1, or
+  // fp32 weights, which the matrix-core path does not take)
   const sl::Plan plan = make_plan(h, dense, y_dtype);
   // With the atomic split reduction y must start at zero: the gate kernel
   // clears it, or a fill kernel does when no gate kernel runs. A product stage
   // run on its own adds onto y as it stands.
   const bool zero = plan.atomic && plan.splits > 1;
-  const bool run_gate = !dense && (stages & SL_STAGE_GATE) &&
-                        (h->gate != SL_GATE_FIXED || mask_out || count_out || thresh_out);
-  const bool full = (stages & SL_STAGE_GATE) && (stages & SL_STAGE_PRODUCT);
-  if (run_gate)
+  if (gate_wanted)
     SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, (zero && full) ? (float*)y : nullptr, s));
   else if (zero && full)
     SL_HIP(sl::launch_zero((float*)y, (int64_t)B * h->m, s));
-  if (stages & SL_STAGE_PRODUCT) SL_HIP(sl::launch_product(h, plan, x, dense, y, y_dtype, s));
+  if (stages & SL_STAGE_PRODUCT) {
+    const size_t xsz = (h->wdt == SL_BF16) ? 2 : 4;
+    for (int b = 0; b < B; ++b)
+      SL_HIP(sl::launch_product(h, plan, (const char*)x + (size_t)b * h->n * xsz, h->gout + b, dense,
+                                (char*)y + (size_t)b * h->m * ysz, y_dtype, s));
+  }
   return SL_OK;
 }
 

@@ -30,6 +30,8 @@ static_assert(sizeof(GateOut) == 24, "GateOut layout");
 // Scratch limits of the single-token product kernel.
 constexpr int kMaxSplits = 1024;   // K-splits per row tile
 constexpr int kMaxChunk = 1024;    // inputs examined per workgroup
+constexpr int kUnionMaxChunk = 512;  // inputs per workgroup of the union product
+constexpr int kUnionMinChunk = 256;  // sizes the union partial buffer
 
 struct Plan {
   int lpc;     // lanes per column run (16, 32 or 64)
@@ -43,9 +45,10 @@ struct Plan {
 
 // Matrix-core (union) product plan.
 struct UnionPlan {
-  int tiles;   // row tiles of 64 rows
+  int tiles;   // row tiles of 128 rows
   int splits;  // input chunks
-  int chunk;   // inputs per chunk (multiple of 32, <= 256)
+  int chunk;   // inputs per chunk (kUnionMinChunk..kUnionMaxChunk unless n is smaller)
+  bool atomic; // fp32 atomic split reduction (else ordered, reproducible)
 };
 
 }  // namespace sl
@@ -84,8 +87,8 @@ hipError_t launch_norms(const void* Wt, sl_dtype dt, int64_t m, int64_t n, float
 hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_out,
                        int32_t* count_out, double* thresh_out, float* zero_y, hipStream_t s);
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
-hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, bool dense, void* y,
-                          sl_dtype ydt, hipStream_t s);
+hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
+                          void* y, sl_dtype ydt, hipStream_t s);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,
                                 bool dense, void* y, sl_dtype ydt, hipStream_t s);
 

@@ -227,28 +227,30 @@ __global__ __launch_bounds__(256) void zero_kernel(float* __restrict__ y, int co
 }
 
 template <typename WT, typename YT, int LPC, bool DENSE, bool ATOMIC>
-hipError_t go(const sl_linear* h, const sl::Plan& p, const void* x, void* y, hipStream_t s) {
+hipError_t go(const sl_linear* h, const sl::Plan& p, const void* x, const sl::GateOut* g, void* y, hipStream_t s) {
   const int grid = p.tiles * p.splits;
   product_kernel<WT, YT, LPC, 8, DENSE, ATOMIC><<<grid, PT, 0, s>>>(
-      (const WT*)h->Wt, (const WT*)x, h->c, h->gout, (int)h->m, (int)h->n, p.tiles, p.splits, p.chunk,
-      h->partials, h->ctr, (YT*)y);
+      (const WT*)h->Wt, (const WT*)x, h->c, g, (int)h->m, (int)h->n, p.tiles, p.splits, p.chunk, h->partials,
+      h->ctr, (YT*)y);
   return hipGetLastError();
 }
 
 template <typename WT, typename YT, bool DENSE, bool ATOMIC>
-hipError_t go_lpc(const sl_linear* h, const sl::Plan& p, const void* x, void* y, hipStream_t s) {
+hipError_t go_lpc(const sl_linear* h, const sl::Plan& p, const void* x, const sl::GateOut* g, void* y,
+                  hipStream_t s) {
   switch (p.lpc) {
-    case 16: return go<WT, YT, 16, DENSE, ATOMIC>(h, p, x, y, s);
-    case 32: return go<WT, YT, 32, DENSE, ATOMIC>(h, p, x, y, s);
-    default: return go<WT, YT, 64, DENSE, ATOMIC>(h, p, x, y, s);
+    case 16: return go<WT, YT, 16, DENSE, ATOMIC>(h, p, x, g, y, s);
+    case 32: return go<WT, YT, 32, DENSE, ATOMIC>(h, p, x, g, y, s);
+    default: return go<WT, YT, 64, DENSE, ATOMIC>(h, p, x, g, y, s);
   }
 }
 
 template <typename WT, bool DENSE>
-hipError_t go_y(const sl_linear* h, const sl::Plan& p, const void* x, void* y, sl_dtype ydt, hipStream_t s) {
-  if (ydt == SL_BF16) return go_lpc<WT, uint16_t, DENSE, false>(h, p, x, y, s);
-  if (p.atomic) return go_lpc<WT, float, DENSE, true>(h, p, x, y, s);
-  return go_lpc<WT, float, DENSE, false>(h, p, x, y, s);
+hipError_t go_y(const sl_linear* h, const sl::Plan& p, const void* x, const sl::GateOut* g, void* y, sl_dtype ydt,
+                hipStream_t s) {
+  if (ydt == SL_BF16) return go_lpc<WT, uint16_t, DENSE, false>(h, p, x, g, y, s);
+  if (p.atomic) return go_lpc<WT, float, DENSE, true>(h, p, x, g, y, s);
+  return go_lpc<WT, float, DENSE, false>(h, p, x, g, y, s);
 }
 
 }  // namespace
@@ -260,12 +262,12 @@ hipError_t launch_zero(float* y, int64_t count, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, bool dense, void* y,
-                          sl_dtype ydt, hipStream_t s) {
+hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
+                          void* y, sl_dtype ydt, hipStream_t s) {
   if (h->wdt == SL_BF16) {
-    return dense ? go_y<uint16_t, true>(h, p, x, y, ydt, s) : go_y<uint16_t, false>(h, p, x, y, ydt, s);
+    return dense ? go_y<uint16_t, true>(h, p, x, g, y, ydt, s) : go_y<uint16_t, false>(h, p, x, g, y, ydt, s);
   }
-  return dense ? go_y<float, true>(h, p, x, y, ydt, s) : go_y<float, false>(h, p, x, y, ydt, s);
+  return dense ? go_y<float, true>(h, p, x, g, y, ydt, s) : go_y<float, false>(h, p, x, g, y, ydt, s);
 }
 
 }  // namespace sl

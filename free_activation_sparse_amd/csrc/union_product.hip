@@ -1,12 +1,259 @@
-// Batched (B > 1) union product on the matrix cores: placeholder until the
-// MFMA kernel lands.
+// Batched product on the matrix cores: for B tokens with their own kept sets,
+//   Y[b][:] = sum over j kept by token b of x_b[j] * W[:, j].
+//
+// Each token keeps its own inputs (WINA article, section 一: per-token gate);
+// the columns of a batch are read once for all of them by running the product
+// over the union U of the B kept sets, with the token-wise input matrix
+// X_U[j][b] = x_b[j] if token b kept j, else 0. The zeros make every token's
+// result exactly its own sparse sum, while W[:, U] X_U is a dense contraction
+// that suits bf16 MFMA (v_mfma_f32_16x16x32_bf16: 16 output rows x 16 tokens
+// x 32 union columns per instruction, fp32 accumulation).
+//
+// Grid: (row tiles of R = 128 rows) x (input chunks). Every workgroup
+//   1. re-evaluates the B predicates for its chunk (x, c and the B gate
+//      pairs), ORs them, compacts the union columns with wavefront ballots and
+//      writes the zero-filled X_U tile to LDS (k-contiguous per token);
+//   2. walks the union in steps of 32 columns: the step's W tile (32 columns
+//      of R contiguous rows, 16-byte loads) goes to LDS in column order with a
+//      padded pitch, and MFMA operands are read back transposed (one row, eight
+//      consecutive union columns per lane) free of bank conflicts; the next
+//      step's tile is loaded while the current one is multiplied;
+//   3. adds its [R][B] partial into Y: fp32 atomics, or the ordered
+//      last-arrival reduction (bit-reproducible; bf16 outputs).
+#include "device_common.h"
 #include "internal.h"
+
+namespace {
+
+using namespace sl::dev;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int UT = 256;             // threads per workgroup (4 wavefronts)
+constexpr int UR = 128;             // rows per tile: 32 per wavefront, two 16-row MFMA blocks
+constexpr int UK = 32;              // union columns per step (one MFMA k-depth)
+constexpr int WPITCH = 2 * UR + 4;  // bytes per staged column: 65 dwords (conflict-free transposed reads)
+constexpr int XPITCH = 2 * sl::kUnionMaxChunk + 16;  // bytes per token row of X_U
+
+__device__ __forceinline__ uint16_t lds_u16(const uint8_t* p) { return *(const uint16_t*)p; }
+
+template <typename YT, bool ATOMIC>
+__global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ x,
+                                                   const float* __restrict__ c,
+                                                   const sl::GateOut* __restrict__ gout, int m, int n, int B,
+                                                   int tiles, int splits, int chunk, bool dense,
+                                                   float* __restrict__ partials, uint32_t* __restrict__ ctr,
+                                                   YT* __restrict__ y) {
+  __shared__ __align__(16) uint8_t ws[2][UK * WPITCH];     // staged W tiles, column-major
+  __shared__ __align__(16) uint8_t xu[16 * XPITCH];        // X_U, [token][k] bf16
+  __shared__ int ulist[sl::kUnionMaxChunk + UK];           // union column indices
+  __shared__ uint32_t wcnt[sl::kUnionMaxChunk / UT][4];
+  __shared__ uint32_t gk[16];
+  __shared__ int gj[16];
+  __shared__ uint32_t s_last;
+
+  const int tile = blockIdx.x % tiles;
+  const int split = blockIdx.x / tiles;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int j0 = split * chunk;
+  const int j1 = min(j0 + chunk, n);
+  const int row0 = tile * UR;
+  constexpr int ROUNDS = sl::kUnionMaxChunk / UT;
+
+  if (t < 16) {
+    gk[t] = (t < B && !dense) ? gout[t].kthr : 0u;
+    gj[t] = (t < B && !dense) ? gout[t].jlast : 0;
+  }
+  __syncthreads();
+
+  // 1. union of the B kept sets over this chunk, and the X_U tile
+  const int nr = (j1 - j0 + UT - 1) / UT;
+  uint32_t tmask[ROUNDS];
+  uint64_t bal[ROUNDS];
+  uint16_t xr[ROUNDS][16];
+  // all loads unconditional (token and input indices clamped) so they are in
+  // flight together; values of tokens >= B are masked out below
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int j = j0 + q * UT + t;
+    const int jc = j < j1 ? j : j1 - 1;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) xr[q][b] = x[(size_t)(b < B ? b : B - 1) * n + jc];
+  }
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int j = j0 + q * UT + t;
+    const int jc = j < j1 ? j : j1 - 1;
+    const float cv = c[jc];
+    uint32_t mk = 0u;
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const float xv = __uint_as_float((uint32_t)xr[q][b] << 16);
+      const bool keep = b < B && (dense || gate_keep(score_key(xv, cv), jc, gk[b], gj[b]));
+      mk |= keep ? (1u << b) : 0u;
+    }
+    tmask[q] = (q < nr && j < j1) ? mk : 0u;
+    bal[q] = __ballot(tmask[q] != 0u);
+    if (lane == 0) wcnt[q][w] = (uint32_t)__popcll(bal[q]);
+  }
+  __syncthreads();
+  int cnt = 0;
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    if (q < nr) {
+      uint32_t off = (uint32_t)cnt;
+      for (int k = 0; k < w; ++k) off += wcnt[q][k];
+      if (tmask[q] != 0u) {
+        const int pos = (int)(off + lanes_below(bal[q]));
+        ulist[pos] = j0 + q * UT + t;
+#pragma unroll
+        for (int b = 0; b < 16; ++b)
+          *(uint16_t*)(xu + b * XPITCH + 2 * pos) = ((tmask[q] >> b) & 1u) ? xr[q][b] : (uint16_t)0;
+      }
+      cnt += (int)(wcnt[q][0] + wcnt[q][1] + wcnt[q][2] + wcnt[q][3]);
+    }
+  }
+  // pad the union to a multiple of UK: column j0 (any valid one) with zero inputs
+  const int cntp = (cnt + UK - 1) / UK * UK;
+  for (int k = cnt + t; k < cntp; k += UT) {
+    ulist[k] = j0;
+    for (int b = 0; b < 16; ++b) *(uint16_t*)(xu + b * XPITCH + 2 * k) = 0;
+  }
+  __syncthreads();
+
+  // 2. stream the union columns' row tiles through LDS into the MFMAs
+  // loader: thread t moves 16 rows-bytes of two columns per step
+  const int lcol = t >> 4;                 // 0..15 (and +16)
+  const int lrow = (t & 15) * 8;           // first of 8 rows
+  const int grow = min(row0 + lrow, m - 8);  // clamped into range; rows >= m are never written
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  const int rb = w * 32;                   // this wavefront's 32 rows inside the tile
+  const int ti = lane & 15;                // token (B operand column) / row within block
+  const int kg = lane >> 4;                // k group of 8
+  u32x4 r0v, r1v;
+  auto gload = [&](int k0) {
+    const int ca = ulist[k0 + lcol], cb = ulist[k0 + lcol + 16];
+    r0v = __builtin_nontemporal_load((const u32x4*)(Wt + (size_t)ca * m + grow));
+    r1v = __builtin_nontemporal_load((const u32x4*)(Wt + (size_t)cb * m + grow));
+  };
+  auto lstore = [&](int buf) {
+    uint32_t* d0 = (uint32_t*)(ws[buf] + lcol * WPITCH + 2 * lrow);
+    uint32_t* d1 = (uint32_t*)(ws[buf] + (lcol + 16) * WPITCH + 2 * lrow);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      d0[q] = r0v[q];
+      d1[q] = r1v[q];
+    }
+  };
+  if (cntp > 0) {
+    gload(0);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int s = 0; s * UK < cntp; ++s) {
+    const int cur = s & 1;
+    const bool more = (s + 1) * UK < cntp;
+    if (more) gload((s + 1) * UK);
+    // B operand: X_U[k = 8*kg .. +8][token ti]
+    const bf16x8 bop = *(const bf16x8*)(xu + ti * XPITCH + 2 * (s * UK + 8 * kg));
+    // A operands: W[row][k = 8*kg + q] for rows rb + ti and rb + 16 + ti
+    bf16x8 a0, a1;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint8_t* col = ws[cur] + (8 * kg + q) * WPITCH;
+      a0[q] = __builtin_bit_cast(__bf16, lds_u16(col + 2 * (rb + ti)));
+      a1[q] = __builtin_bit_cast(__bf16, lds_u16(col + 2 * (rb + 16 + ti)));
+    }
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bop, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bop, acc1, 0, 0, 0);
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // 3. partial [rows][tokens] of this chunk into Y. Lane holds rows
+  //    rb + {0,16} + 4*kg + q for token ti.
+  const int tok = ti;
+  const bool tok_ok = tok < B;
+  if (splits == 1 || ATOMIC) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4 a = h ? acc1 : acc0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = row0 + rb + 16 * h + 4 * kg + q;
+        if (tok_ok && row < m) {
+          if (splits == 1)
+            store_out(y + (size_t)tok * m + row, a[q]);
+          else
+            atomicAdd((float*)(y + (size_t)tok * m + row), a[q]);
+        }
+      }
+    }
+    return;
+  }
+  // ordered reduction: device-coherent partial stores [split][token][row], the
+  // last arrival of the tile adds them in split order
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const f32x4 a = h ? acc1 : acc0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = row0 + rb + 16 * h + 4 * kg + q;
+      if (tok_ok && row < m)
+        __hip_atomic_store(partials + ((size_t)split * B + tok) * m + row, a[q], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (t == 0)
+    s_last = (__hip_atomic_fetch_add(&ctr[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+              (uint32_t)(splits - 1))
+                 ? 1u
+                 : 0u;
+  __syncthreads();
+  if (s_last == 0u) return;
+  for (int e = t; e < UR * B; e += UT) {
+    const int tk = e / UR, row = row0 + e % UR;
+    if (row < m) {
+      float s = 0.f;
+      const float* pp = partials + (size_t)tk * m + row;
+      int k = 0;
+      for (; k + 7 < splits; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = __hip_atomic_load(pp + (size_t)(k + u) * B * m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+      }
+      for (; k < splits; ++k)
+        s += __hip_atomic_load(pp + (size_t)k * B * m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_out(y + (size_t)tk * m + row, s);
+    }
+  }
+  if (t == 0) __hip_atomic_store(&ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename YT, bool ATOMIC>
+hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
+              hipStream_t s) {
+  union_kernel<YT, ATOMIC><<<p.tiles * p.splits, UT, 0, s>>>(
+      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
+      p.chunk, dense, h->upartials, h->uctr, (YT*)y);
+  return hipGetLastError();
+}
+
+}  // namespace
 
 namespace sl {
 
-hipError_t launch_union_product(const sl_linear*, const UnionPlan&, const void*, int, bool, void*, sl_dtype,
-                                hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B, bool dense, void* y,
+                                sl_dtype ydt, hipStream_t s) {
+  if (ydt == SL_BF16) return go<uint16_t, false>(h, p, x, B, dense, y, s);
+  if (p.atomic) return go<float, true>(h, p, x, B, dense, y, s);
+  return go<float, false>(h, p, x, B, dense, y, s);
 }
 
 }  // namespace sl
