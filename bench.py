@@ -48,6 +48,9 @@ def parse():
                     help="restrict the measured legs (short profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for memory counters)")
+    ap.add_argument("--workload", default="llama7b_down",
+                    choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16"],
+                    help="llama7b_down is the headline; the others measure the remaining layer shapes")
     return ap.parse_args()
 
 
@@ -78,6 +81,10 @@ def main():
               "(the sparse linear is measured per GPU; see DESIGN.md for how it would shard)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "llama7b_down":
+        run_workload(args)
+        return
 
     import numpy as np
     import torch
@@ -300,6 +307,179 @@ def main():
             out["legs"][k]["speedup_bar"] = round(bar, 4)
     out["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(out))
+
+
+# ---------------------------------------------------------------------------
+# Other layer shapes: a step is one forward of every linear of the workload for
+# a batch of B tokens (ring copies of the weights so that >= 1 GiB rotates).
+# ---------------------------------------------------------------------------
+def workload_legs(name):
+    """[(leg name, B, [(cfg, linear, gate kwargs), ...])]"""
+    import workloads as wl
+    if name == "llama3_block":
+        ps = wl.component_sparsities(3)
+        lins = [(3, li, dict(gate="topk", K=wl.k_from_sparsity(l.n, round(ps[li], 6))))
+                for li, l in enumerate(wl.CONFIGS[3].linears)]
+        return [("block", 1, lins)]
+    if name == "phi4_ffn_stat":
+        lins = [(4, li, dict(gate="stat", s_keep=0.10)) for li in range(3)]
+        return [(f"B{b}", b, lins) for b in (1, 2, 4, 8)]
+    if name == "qwen_ffn_b16":
+        legs = []
+        for p in (0.65, 0.90):
+            lins = [(5, li, dict(gate="topk", K=wl.k_from_sparsity(wl.CONFIGS[5].linears[li].n, p)))
+                    for li in range(3)]
+            legs.append((f"p{int(p * 100)}", 16, lins))
+        return legs
+    raise ValueError(name)
+
+
+def run_workload(args):
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    legs = workload_legs(args.workload)
+    NT = 48  # token batches rotated through
+    host_w = {}
+
+    def dev_bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    results = {}
+    for leg, B, lins in legs:
+        total = sum(wl.CONFIGS[cfg].linears[li].m * wl.CONFIGS[cfg].linears[li].n * 2 for cfg, li, _ in lins)
+        R = max(2, -(-(1 << 30) // total))
+        rings, Xs, Ys, dims = [], [], [], []
+        for cfg, li, gk in lins:
+            lin = wl.CONFIGS[cfg].linears[li]
+            if (cfg, li) not in host_w:
+                host_w[(cfg, li)] = wl.weight(cfg, li)
+            Wd = dev_bf16(host_w[(cfg, li)])
+            rings.append([fas.SparseLinear(Wd, c=None, max_batch=B, **gk) for _ in range(R)])
+            del Wd
+            toks = np.stack([wl.tokens(cfg, li, t * B, B) for t in range(NT)])
+            Xs.append(dev_bf16(toks).reshape(NT, B, lin.n).contiguous())
+            Ys.append(torch.empty((R, B, lin.m), dtype=torch.float32, device=dev))
+            dims.append((lin.name, lin.m, lin.n))
+
+        def step(i, s, stages=3):
+            for L in range(len(lins)):
+                h = rings[L][i % R]
+                fas.sparse_linear_forward_stages(h.handle, Xs[L][i % NT].data_ptr(), B, Ys[L][i % R].data_ptr(),
+                                                 fas.SL_F32, 0, 0, 0, stages, s.cuda_stream)
+
+        secs = _replay_timed(torch, step, args.steps, args.warmup)
+        # untimed side pass: kept (B = 1) or union (B > 1) column counts per linear
+        kept = []
+        for L, (name, m, n) in enumerate(dims):
+            mk = torch.empty((B, n), dtype=torch.uint8, device=dev)
+            tot = 0
+            for t in range(NT):
+                fas.sparse_linear_forward(rings[L][0].handle, Xs[L][t].data_ptr(), B, Ys[L][0].data_ptr(),
+                                          fas.SL_F32, mk.data_ptr(), 0, 0, torch.cuda.current_stream().cuda_stream)
+                tot += int(mk.bool().any(dim=0).sum().item())
+            kept.append(tot / NT)
+        # per-linear kernel times: ring copy r keeps the selection of token batch r
+        prod_us, gate_us = [], []
+        for L in range(len(lins)):
+            s0 = torch.cuda.current_stream()
+            for r in range(R):
+                fas.sparse_linear_forward(rings[L][r].handle, Xs[L][r].data_ptr(), B, Ys[L][r].data_ptr(),
+                                          fas.SL_F32, 0, 0, 0, s0.cuda_stream)
+
+            def one(bit, L=L):
+                def f(i, s):
+                    r = i % R
+                    fas.sparse_linear_forward_stages(rings[L][r].handle, Xs[L][r].data_ptr(), B,
+                                                     Ys[L][r].data_ptr(), fas.SL_F32, 0, 0, 0, bit, s.cuda_stream)
+                return f
+            gate_us.append(_graph_us(torch, one(fas.SL_STAGE_GATE)))
+            prod_us.append(_graph_us(torch, one(fas.SL_STAGE_PRODUCT)))
+        lin_rows = []
+        tot_bytes = 0
+        for L, (name, m, n) in enumerate(dims):
+            ab = kept[L] * m * 2 + B * n * 2 + n * 4 + B * m * 4
+            tot_bytes += ab
+            lin_rows.append({"linear": name, "m": m, "n": n, "columns_read": round(kept[L], 1),
+                             "gate_us": round(gate_us[L], 3), "product_us": round(prod_us[L], 3),
+                             "product_GBps": round(ab / (prod_us[L] * 1e-6) / 1e9, 1)})
+        results[leg] = {"B": B, "tokens_per_s": B * args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
+                        "product_us_sum": sum(prod_us), "product_bytes_sum": tot_bytes,
+                        "product_GBps": tot_bytes / (sum(prod_us) * 1e-6) / 1e9,
+                        "dense_weight_bytes": total, "ring_copies": R, "linears": lin_rows}
+        for ring in rings:
+            for h in ring:
+                h.close()
+        del rings, Xs, Ys
+        torch.cuda.empty_cache()
+
+    first = legs[0][0]
+    head = results[first]
+    out = {
+        "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": {"workload": args.workload, "headline_leg": first, "launch": "graph"},
+        "roofline": {"bound": "hbm", "achieved": round(head["product_GBps"], 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["product_GBps"] / PEAK_GBS, 4), "traffic": None,
+                     "kernel": "product kernels of one step (summed bytes / summed durations)"},
+        "cpu_baseline": None,
+        "legs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                 for k, v in results.items()},
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out))
+
+
+def _replay_timed(torch, f, steps, warmup, G=60):
+    """Warm up, then time exactly `steps` calls of f(i, stream) replayed from
+    HIP graphs of G calls; returns seconds."""
+    cache = {}
+
+    def graph_of(count):
+        if count not in cache:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                s = torch.cuda.current_stream()
+                for i in range(count):
+                    f(i, s)
+            cache[count] = g
+        return cache[count]
+    full, tail = divmod(steps, G)
+    wfull, wtail = divmod(warmup, G)
+    plan_warm = [G] * wfull + ([wtail] if wtail else [])
+    plan_timed = [G] * full + ([tail] if tail else [])
+    for cnt in set(plan_warm + plan_timed):
+        graph_of(cnt)
+    for cnt in plan_warm:
+        cache[cnt].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for cnt in plan_timed:
+        cache[cnt].replay()
+    torch.cuda.synchronize()
+    return time.perf_counter() - t0
+
+
+def _graph_us(torch, fn, count=240):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        for i in range(count):
+            fn(i, s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
 
 
 def cpu_baseline(wl, Wh, K, seconds):
