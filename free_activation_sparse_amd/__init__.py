@@ -29,6 +29,7 @@ EXPORTED = [
     "sparse_linear_get_norms", "sparse_linear_destroy", "sparse_linear_strerror",
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
+    "sparse_linear_set_union_plan",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_forward_stages.restype = ctypes.c_int
     L.sparse_linear_set_deterministic.argtypes = [_vp, _i32]
     L.sparse_linear_set_deterministic.restype = ctypes.c_int
+    L.sparse_linear_set_union_plan.argtypes = [_vp, _i32, _i32]
+    L.sparse_linear_set_union_plan.restype = ctypes.c_int
     L.sparse_linear_set_plan.argtypes = [_vp, _i32, _i32]
     L.sparse_linear_set_plan.restype = ctypes.c_int
     _lib = L
@@ -134,6 +137,10 @@ def sparse_linear_forward_stages(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype
 
 def sparse_linear_set_deterministic(h: int, on: bool) -> None:
     _check(lib().sparse_linear_set_deterministic(h, 1 if on else 0), "sparse_linear_set_deterministic")
+
+
+def sparse_linear_set_union_plan(h: int, rows_per_tile: int, workgroups: int) -> None:
+    _check(lib().sparse_linear_set_union_plan(h, rows_per_tile, workgroups), "sparse_linear_set_union_plan")
 
 
 def sparse_linear_set_plan(h: int, rows_per_tile: int, splits: int) -> None:
@@ -218,6 +225,9 @@ class SparseLinear:
 
     def set_plan(self, rows_per_tile: int = 0, splits: int = 0):
         sparse_linear_set_plan(self.handle, rows_per_tile, splits)
+
+    def set_union_plan(self, rows_per_tile: int = 0, workgroups: int = 0):
+        sparse_linear_set_union_plan(self.handle, rows_per_tile, workgroups)
 
     def set_deterministic(self, on: bool = True):
         sparse_linear_set_deterministic(self.handle, on)

@@ -142,9 +142,10 @@ int max_union_splits(int64_t n) { return (int)std::max<int64_t>(1, (n + sl::kUni
 sl::UnionPlan make_union_plan(const sl_linear* h, sl_dtype ydt) {
   sl::UnionPlan p;
   p.atomic = (ydt == SL_F32) && !h->deterministic;
-  p.tiles = (int)((h->m + 127) / 128);
+  p.rows = (h->uplan_rows == 128 || h->uplan_rows == 256) ? h->uplan_rows : 256;
+  p.tiles = (int)((h->m + p.rows - 1) / p.rows);
   const int64_t n = h->n;
-  int splits = (int)std::max<int64_t>(1, 1536 / p.tiles);
+  int splits = (int)std::max<int64_t>(1, (h->uplan_wgs > 0 ? h->uplan_wgs : 1024) / p.tiles);
   splits = std::min(splits, max_union_splits(n));
   splits = std::max<int>(splits, (int)((n + sl::kUnionMaxChunk - 1) / sl::kUnionMaxChunk));
   p.chunk = (int)((n + splits - 1) / splits);
@@ -264,7 +265,7 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
       h->upart_len = (int64_t)max_union_splits(n) * max_batch * m;
       if ((e = hipMalloc(&h->upartials, (size_t)h->upart_len * sizeof(float))) != hipSuccess)
         return cleanup_fail(e, "hipMalloc(union partials)");
-      const size_t uc = (size_t)((m + 127) / 128);
+      const size_t uc = (size_t)((m + 127) / 128);  // tiles of >= 128 rows
       if ((e = hipMalloc(&h->uctr, uc * sizeof(uint32_t))) != hipSuccess)
         return cleanup_fail(e, "hipMalloc(union counters)");
       if ((e = hipMemsetAsync(h->uctr, 0, uc * sizeof(uint32_t), s)) != hipSuccess)
@@ -399,6 +400,16 @@ sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, vo
   } catch (...) {
     return fail(SL_ERR_OOM, "unexpected host exception in forward_stages");
   }
+}
+
+sl_status sparse_linear_set_union_plan(sl_handle h, int32_t rows_per_tile, int32_t workgroups) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  if (rows_per_tile != 0 && rows_per_tile != 128 && rows_per_tile != 256)
+    return fail(SL_ERR_ARG, "rows_per_tile=%d must be 0, 128 or 256", (int)rows_per_tile);
+  if (workgroups < 0) return fail(SL_ERR_ARG, "workgroups=%d must be >= 0", (int)workgroups);
+  h->uplan_rows = rows_per_tile;
+  h->uplan_wgs = workgroups;
+  return SL_OK;
 }
 
 sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on) {

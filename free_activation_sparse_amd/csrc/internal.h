@@ -45,7 +45,8 @@ struct Plan {
 
 // Matrix-core (union) product plan.
 struct UnionPlan {
-  int tiles;   // row tiles of 128 rows
+  int rows;    // rows per tile: 128 or 256
+  int tiles;   // row tiles
   int splits;  // input chunks
   int chunk;   // inputs per chunk (kUnionMinChunk..kUnionMaxChunk unless n is smaller)
   bool atomic; // fp32 atomic split reduction (else ordered, reproducible)
@@ -75,6 +76,7 @@ struct sl_linear {
   uint32_t* uctr = nullptr;     // [utiles]
 
   int plan_rows = 0, plan_splits = 0;  // overrides (0 = automatic)
+  int uplan_rows = 0, uplan_wgs = 0;   // union-product overrides (0 = automatic)
   bool deterministic = false;          // ordered split reduction for fp32 y too
 
 };

@@ -9,15 +9,15 @@
 // that suits bf16 MFMA (v_mfma_f32_16x16x32_bf16: 16 output rows x 16 tokens
 // x 32 union columns per instruction, fp32 accumulation).
 //
-// Grid: (row tiles of R = 128 rows) x (input chunks). Every workgroup
+// Grid: (row tiles of R = 128 or 256 rows) x (input chunks). Every workgroup
 //   1. re-evaluates the B predicates for its chunk (x, c and the B gate
 //      pairs), ORs them, compacts the union columns with wavefront ballots and
 //      writes the zero-filled X_U tile to LDS (k-contiguous per token);
 //   2. walks the union in steps of 32 columns: the step's W tile (32 columns
 //      of R contiguous rows, 16-byte loads) goes to LDS in column order with a
 //      padded pitch, and MFMA operands are read back transposed (one row, eight
-//      consecutive union columns per lane) free of bank conflicts; the next
-//      step's tile is loaded while the current one is multiplied;
+//      consecutive union columns per lane) free of bank conflicts; the loads
+//      of the next D steps are in flight while the current one is multiplied;
 //   3. adds its [R][B] partial into Y: fp32 atomics, or the ordered
 //      last-arrival reduction (bit-reproducible; bf16 outputs).
 #include "device_common.h"
@@ -31,20 +31,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int UT = 256;             // threads per workgroup (4 wavefronts)
-constexpr int UR = 128;             // rows per tile: 32 per wavefront, two 16-row MFMA blocks
 constexpr int UK = 32;              // union columns per step (one MFMA k-depth)
-constexpr int WPITCH = 2 * UR + 4;  // bytes per staged column: 65 dwords (conflict-free transposed reads)
 constexpr int XPITCH = 2 * sl::kUnionMaxChunk + 16;  // bytes per token row of X_U
 
 __device__ __forceinline__ uint16_t lds_u16(const uint8_t* p) { return *(const uint16_t*)p; }
 
-template <typename YT, bool ATOMIC>
+// NB: 16-row MFMA blocks per wavefront (tile of R = 64 * NB rows); D: column
+// steps whose loads are in flight ahead of the one being multiplied.
+template <typename YT, bool ATOMIC, int NB, int D>
 __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ x,
                                                    const float* __restrict__ c,
                                                    const sl::GateOut* __restrict__ gout, int m, int n, int B,
                                                    int tiles, int splits, int chunk, bool dense,
                                                    float* __restrict__ partials, uint32_t* __restrict__ ctr,
                                                    YT* __restrict__ y) {
+  constexpr int UR = 64 * NB;          // rows per tile
+  // bytes per staged column: R/2 + 1 dwords (1 mod 4), so the four 8-column
+  // groups of a transposed operand read land on disjoint LDS banks
+  constexpr int WPITCH = 2 * UR + 4;
   __shared__ __align__(16) uint8_t ws[2][UK * WPITCH];     // staged W tiles, column-major
   __shared__ __align__(16) uint8_t xu[16 * XPITCH];        // X_U, [token][k] bf16
   __shared__ int ulist[sl::kUnionMaxChunk + UK];           // union column indices
@@ -122,71 +126,88 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   }
   __syncthreads();
 
-  // 2. stream the union columns' row tiles through LDS into the MFMAs
-  // loader: thread t moves 16 rows-bytes of two columns per step
-  const int lcol = t >> 4;                 // 0..15 (and +16)
-  const int lrow = (t & 15) * 8;           // first of 8 rows
-  const int grow = min(row0 + lrow, m - 8);  // clamped into range; rows >= m are never written
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  const int rb = w * 32;                   // this wavefront's 32 rows inside the tile
-  const int ti = lane & 15;                // token (B operand column) / row within block
-  const int kg = lane >> 4;                // k group of 8
-  u32x4 r0v, r1v;
-  auto gload = [&](int k0) {
-    const int ca = ulist[k0 + lcol], cb = ulist[k0 + lcol + 16];
-    r0v = __builtin_nontemporal_load((const u32x4*)(Wt + (size_t)ca * m + grow));
-    r1v = __builtin_nontemporal_load((const u32x4*)(Wt + (size_t)cb * m + grow));
-  };
-  auto lstore = [&](int buf) {
-    uint32_t* d0 = (uint32_t*)(ws[buf] + lcol * WPITCH + 2 * lrow);
-    uint32_t* d1 = (uint32_t*)(ws[buf] + (lcol + 16) * WPITCH + 2 * lrow);
+  // 2. stream the union columns' row tiles through LDS into the MFMAs. Thread
+  //    t moves NB 16-byte vectors per step: vector v = t + UT * i covers rows
+  //    8 * (v mod R/8) .. +8 of step column v / (R/8).
+  constexpr int VPC = UR / 8;  // 16-byte vectors per column run
+  int lcol[NB], lrow[NB];
+  const uint16_t* gsrc[NB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      d0[q] = r0v[q];
-      d1[q] = r1v[q];
-    }
-  };
-  if (cntp > 0) {
-    gload(0);
-    lstore(0);
+  for (int i = 0; i < NB; ++i) {
+    const int v = t + UT * i;
+    lcol[i] = v / VPC;
+    lrow[i] = (v % VPC) * 8;
+    // clamped into range; rows >= m are loaded from row m - 8 and never written
+    gsrc[i] = Wt + min(row0 + lrow[i], m - 8);
   }
-  __syncthreads();
-  for (int s = 0; s * UK < cntp; ++s) {
-    const int cur = s & 1;
-    const bool more = (s + 1) * UK < cntp;
-    if (more) gload((s + 1) * UK);
-    // B operand: X_U[k = 8*kg .. +8][token ti]
-    const bf16x8 bop = *(const bf16x8*)(xu + ti * XPITCH + 2 * (s * UK + 8 * kg));
-    // A operands: W[row][k = 8*kg + q] for rows rb + ti and rb + 16 + ti
-    bf16x8 a0, a1;
+  f32x4 acc[NB];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const uint8_t* col = ws[cur] + (8 * kg + q) * WPITCH;
-      a0[q] = __builtin_bit_cast(__bf16, lds_u16(col + 2 * (rb + ti)));
-      a1[q] = __builtin_bit_cast(__bf16, lds_u16(col + 2 * (rb + 16 + ti)));
+  for (int h = 0; h < NB; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rb = w * 16 * NB;  // this wavefront's rows inside the tile
+  const int ti = lane & 15;    // token (B operand column) / row within block
+  const int kg = lane >> 4;    // k group of 8
+  const int nsteps = cntp / UK;
+  u32x4 pr[D][NB];             // ring of prefetched steps: step q lives in slot q % D
+  auto gload = [&](int slot, int q) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int col = ulist[q * UK + lcol[i]];
+      pr[slot][i] = __builtin_nontemporal_load((const u32x4*)(gsrc[i] + (size_t)col * m));
     }
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, bop, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, bop, acc1, 0, 0, 0);
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
+  };
+  auto lstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      uint32_t* d = (uint32_t*)(ws[buf] + lcol[i] * WPITCH + 2 * lrow[i]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) d[q] = pr[slot][i][q];
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nsteps) gload(d, d);
+  if (nsteps > 0) lstore(0, 0);
+  __syncthreads();
+  if (D < nsteps) gload(0, D);
+  for (int s0 = 0; s0 < nsteps; s0 += D) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int s = s0 + u;  // s % D == u
+      if (s < nsteps) {
+        // B operand: X_U[k = 8*kg .. +8][token ti]
+        const bf16x8 bop = *(const bf16x8*)(xu + ti * XPITCH + 2 * (s * UK + 8 * kg));
+        const uint8_t* wb = ws[s & 1];
+#pragma unroll
+        for (int h = 0; h < NB; ++h) {
+          // A operand: W[row rb + 16h + ti][k = 8*kg + q]
+          bf16x8 a;
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            a[q] = __builtin_bit_cast(__bf16, lds_u16(wb + (8 * kg + q) * WPITCH + 2 * (rb + 16 * h + ti)));
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop, acc[h], 0, 0, 0);
+        }
+        if (s + 1 < nsteps) lstore((u + 1) % D, (s + 1) & 1);
+        __syncthreads();
+        if (s + 1 + D < nsteps) gload((u + 1) % D, s + 1 + D);
+      }
+    }
   }
 
   // 3. partial [rows][tokens] of this chunk into Y. Lane holds rows
-  //    rb + {0,16} + 4*kg + q for token ti.
+  //    rb + 16h + 4*kg + q for token ti.
   const int tok = ti;
   const bool tok_ok = tok < B;
   if (splits == 1 || ATOMIC) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4 a = h ? acc1 : acc0;
+    for (int h = 0; h < NB; ++h) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = row0 + rb + 16 * h + 4 * kg + q;
         if (tok_ok && row < m) {
           if (splits == 1)
-            store_out(y + (size_t)tok * m + row, a[q]);
+            store_out(y + (size_t)tok * m + row, acc[h][q]);
           else
-            atomicAdd((float*)(y + (size_t)tok * m + row), a[q]);
+            atomicAdd((float*)(y + (size_t)tok * m + row), acc[h][q]);
         }
       }
     }
@@ -195,13 +216,12 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   // ordered reduction: device-coherent partial stores [split][token][row], the
   // last arrival of the tile adds them in split order
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const f32x4 a = h ? acc1 : acc0;
+  for (int h = 0; h < NB; ++h) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int row = row0 + rb + 16 * h + 4 * kg + q;
       if (tok_ok && row < m)
-        __hip_atomic_store(partials + ((size_t)split * B + tok) * m + row, a[q], __ATOMIC_RELAXED,
+        __hip_atomic_store(partials + ((size_t)split * B + tok) * m + row, acc[h][q], __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -236,13 +256,20 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   if (t == 0) __hip_atomic_store(&ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <typename YT, bool ATOMIC>
-hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
-              hipStream_t s) {
-  union_kernel<YT, ATOMIC><<<p.tiles * p.splits, UT, 0, s>>>(
+template <typename YT, bool ATOMIC, int NB, int D>
+hipError_t go_nd(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
+                 hipStream_t s) {
+  union_kernel<YT, ATOMIC, NB, D><<<p.tiles * p.splits, UT, 0, s>>>(
       (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
       p.chunk, dense, h->upartials, h->uctr, (YT*)y);
   return hipGetLastError();
+}
+
+template <typename YT, bool ATOMIC>
+hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
+              hipStream_t s) {
+  if (p.rows == 256) return go_nd<YT, ATOMIC, 4, 3>(h, p, x, B, dense, y, s);
+  return go_nd<YT, ATOMIC, 2, 4>(h, p, x, B, dense, y, s);
 }
 
 }  // namespace

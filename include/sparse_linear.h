@@ -178,6 +178,13 @@ sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on);
  */
 sl_status sparse_linear_set_plan(sl_handle h, int32_t rows_per_tile, int32_t splits);
 
+/*
+ * Launch-shape override of the batched (B > 1, bf16) union product:
+ * rows_per_tile in {128, 256} (0 = automatic) and the target number of
+ * workgroups (0 = automatic; input chunks stay within 256..512).
+ */
+sl_status sparse_linear_set_union_plan(sl_handle h, int32_t rows_per_tile, int32_t workgroups);
+
 #ifdef __cplusplus
 }
 #endif
