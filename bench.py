@@ -3,8 +3,10 @@
 Workload: the Llama-2-7B-shaped FFN down projection, W 4096 x 11008 bf16
 (std 0.02), x = SiLU(g) * u with g, u ~ N(0, 1) rounded to bf16, one token per
 step (batch-1 decode), WINA top-K at 50 % sparsity (K = 5504, the headline) and
-65 % sparsity (K = 3853). A step is one full forward: the gate kernel (scores,
-top-K select) and the product kernel (predicate, compaction, gather-GEMV).
+65 % sparsity (K = 3853). A step is one full forward, one fused launch: a gate
+workgroup (scores, top-K select) and the product workgroups (predicate,
+compaction, gather-GEMV). The two-launch form (gate kernel, then product
+kernel) is timed beside it.
 
 Weights rotate through 12 handle-owned copies (1.08 GB) so the 256 MB
 Infinity Cache never serves them; tokens rotate through 256 seeded tokens held
@@ -12,10 +14,11 @@ in HBM. Steps are captured into HIP graphs and replayed, so the host's per-call
 overhead does not throttle the GPU; the timed region is bracketed by
 torch.cuda.synchronize().
 
-Printed: one JSON line with tokens/s, ms per step, the product kernel's
+Printed: one JSON line with tokens/s, ms per step, the fused kernel's
 achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak (its
-duration from HIP events around each launch), the same-kernel dense baseline,
-hipBLASLt's dense GEMV for context, and the CPU oracle timed on the host.
+duration from HIP events on its stream around back-to-back launches), the
+same-kernel dense baseline, hipBLASLt's dense GEMV for context, and the CPU
+oracle timed on the host.
 """
 from __future__ import annotations
 
@@ -55,22 +58,35 @@ def parse():
 
 
 def algorithmic_bytes(m, n, K, B=1):
-    """Bytes one product launch must move: the kept columns (K*m bf16), x and c
-    for every input (n*(2+4)), and y (m fp32)."""
+    """Bytes one forward must move: the kept columns (K*m bf16), x and c for
+    every input (n*(2+4)), and y (m fp32)."""
     return K * m * 2 + B * n * 2 + n * 4 + B * m * 4
 
 
-def traffic_from_profile(kernel_src):
-    """HBM bytes per product launch from the committed memory-counter summary,
-    or None when the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "product_kernel_memory_counters.md")
+FUSED_SOURCES = ["fused.hip", "gate_body.h", "product_body.h", "device_common.h"]
+
+
+def sources_sha256(names):
+    """sha256 over the named kernel sources, in order (identifies the build the
+    memory counters were taken from)."""
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "free_activation_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def traffic_from_profile(kernel, sources, K):
+    """HBM bytes per launch of `kernel` from the committed memory-counter
+    summary, or None when its sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_memory_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source sha256: ([0-9a-f]{64})", text)
-    if not m or m.group(1) != hashlib.sha256(open(kernel_src, "rb").read()).hexdigest():
+    if not m or m.group(1) != sources_sha256(sources):
         return None
-    t = re.search(r"bytes per launch \(K=5504\): (\d+)", text)
+    t = re.search(r"bytes per launch \(K=%d\): (\d+)" % K, text)
     return int(t.group(1)) if t else None
 
 
@@ -177,11 +193,17 @@ def main():
         return e0.elapsed_time(e1) * 1e3 / count
 
     def kernel_times(ring, dense):
-        """(gate us, product us): each kernel launched alone, back to back. Ring
-        copy i keeps the selection of token i, so the product-only launches move
-        exactly the bytes of a full forward."""
+        """(gate us, product us, fused us, two-launch us). The fused launch and
+        the two-launch forward are timed whole; the gate and product kernels of
+        the two-launch form are also launched alone, back to back (ring copy i
+        keeps the selection of token i, so the product-only launches move
+        exactly the bytes of a full forward)."""
         if dense:
-            return 0.0, time_graph(layer_step(ring, True))
+            return 0.0, time_graph(layer_step(ring, True)), None, None
+        fused_us = time_graph(layer_step(ring, False))
+        for h in ring:
+            h.set_fused(False)
+        two_us = time_graph(layer_step(ring, False))
         s0 = torch.cuda.current_stream()
         for i in range(RING):
             fas.sparse_linear_forward(ring[i].handle, X[i].data_ptr(), 1, Y[i].data_ptr(), fas.SL_F32,
@@ -195,7 +217,9 @@ def main():
             return f
         gate_us = time_graph(stage(fas.SL_STAGE_GATE))
         prod_us = time_graph(stage(fas.SL_STAGE_PRODUCT))
-        return gate_us, prod_us
+        for h in ring:
+            h.set_fused(True)
+        return gate_us, prod_us, fused_us, two_us
 
     results = {}
     legs = ["sparse50", "sparse65"] if args.only == "all" else ([args.only] if args.only != "dense" else [])
@@ -203,15 +227,19 @@ def main():
         K = Ks[leg]
         ring = make_ring(K)
         secs = run_steps(layer_step(ring, False), args.steps, args.warmup)
-        gate_us, prod_us = kernel_times(ring, False)
+        gate_us, prod_us, fused_us, two_us = kernel_times(ring, False)
+        for h in ring:
+            h.sync_status()
         ab = algorithmic_bytes(m, n, K)
         results[leg] = {
             "K": K, "sparsity": 1 - K / n,
             "tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
-            "gate_kernel_us": gate_us, "product_kernel_us": prod_us,
-            "product_algorithmic_bytes": ab,
-            "product_achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
+            "fused_kernel_us": fused_us, "algorithmic_bytes": ab,
+            "fused_achieved_GBps": ab / (fused_us * 1e-6) / 1e9,
             "step_achieved_GBps": ab / (secs / args.steps) / 1e9,
+            "two_launch_us_per_step": two_us,
+            "gate_kernel_us": gate_us, "product_kernel_us": prod_us,
+            "product_achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
         }
         for h in ring:
             h.close()
@@ -221,7 +249,7 @@ def main():
     if args.only in ("all", "dense"):
         ring = make_ring(Ks["sparse50"])
         secs = run_steps(layer_step(ring, True), args.steps, args.warmup)
-        _, prod_us = kernel_times(ring, True)
+        _, prod_us, _, _ = kernel_times(ring, True)
         ab = algorithmic_bytes(m, n, n)
         dense = {"tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
                  "product_kernel_us": prod_us, "achieved_GBps": ab / (prod_us * 1e-6) / 1e9}
@@ -286,15 +314,14 @@ def main():
     if head:
         out["roofline"] = {
             "bound": "hbm",
-            "achieved": round(head["product_achieved_GBps"], 1),
+            "achieved": round(head["fused_achieved_GBps"], 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(head["product_achieved_GBps"] / PEAK_GBS, 4),
-            "traffic": traffic_from_profile(os.path.join(ROOT, "free_activation_sparse_amd", "csrc",
-                                                         "product.hip")),
-            "kernel": "product_kernel (gather-GEMV)",
-            "kernel_us": round(head["product_kernel_us"], 3),
-            "algorithmic_bytes": head["product_algorithmic_bytes"],
+            "frac": round(head["fused_achieved_GBps"] / PEAK_GBS, 4),
+            "traffic": traffic_from_profile("fused_kernel", FUSED_SOURCES, Ks["sparse50"]),
+            "kernel": "fused_kernel (gate workgroup + gather-GEMV workgroups)",
+            "kernel_us": round(head["fused_kernel_us"], 3),
+            "algorithmic_bytes": head["algorithmic_bytes"],
         }
     out["cpu_baseline"] = cpu
     out["legs"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}

@@ -29,7 +29,7 @@ EXPORTED = [
     "sparse_linear_get_norms", "sparse_linear_destroy", "sparse_linear_strerror",
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
-    "sparse_linear_set_union_plan",
+    "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -77,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_set_union_plan.restype = ctypes.c_int
     L.sparse_linear_set_plan.argtypes = [_vp, _i32, _i32]
     L.sparse_linear_set_plan.restype = ctypes.c_int
+    L.sparse_linear_set_fused.argtypes = [_vp, _i32]
+    L.sparse_linear_set_fused.restype = ctypes.c_int
+    L.sparse_linear_sync_status.argtypes = [_vp, _vp]
+    L.sparse_linear_sync_status.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -145,6 +149,14 @@ def sparse_linear_set_union_plan(h: int, rows_per_tile: int, workgroups: int) ->
 
 def sparse_linear_set_plan(h: int, rows_per_tile: int, splits: int) -> None:
     _check(lib().sparse_linear_set_plan(h, rows_per_tile, splits), "sparse_linear_set_plan")
+
+
+def sparse_linear_set_fused(h: int, on: bool) -> None:
+    _check(lib().sparse_linear_set_fused(h, 1 if on else 0), "sparse_linear_set_fused")
+
+
+def sparse_linear_sync_status(h: int, stream: int = 0) -> None:
+    _check(lib().sparse_linear_sync_status(h, stream), "sparse_linear_sync_status")
 
 
 # ------------------------------------------------------------------ torch wrapper
@@ -231,6 +243,13 @@ class SparseLinear:
 
     def set_deterministic(self, on: bool = True):
         sparse_linear_set_deterministic(self.handle, on)
+
+    def set_fused(self, on: bool = True):
+        sparse_linear_set_fused(self.handle, on)
+
+    def sync_status(self):
+        """Synchronize the current stream; raise if a fused hand-off timed out."""
+        sparse_linear_sync_status(self.handle, self._stream())
 
     def close(self):
         if getattr(self, "handle", None):

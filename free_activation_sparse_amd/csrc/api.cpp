@@ -169,6 +169,7 @@ void free_handle(sl_linear* h) {
   (void)hipFree(h->ctr);
   (void)hipFree(h->upartials);
   (void)hipFree(h->uctr);
+  (void)hipFree(h->fsync);
   delete h;
 }
 
@@ -260,6 +261,11 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
       return cleanup_fail(e, "hipMalloc(counters)");
     if ((e = hipMemsetAsync(h->ctr, 0, (size_t)h->ctr_len * sizeof(uint32_t), s)) != hipSuccess)
       return cleanup_fail(e, "hipMemsetAsync(counters)");
+    if ((e = hipMalloc(&h->fsync, sizeof(sl::FusedSync))) != hipSuccess) return cleanup_fail(e, "hipMalloc(sync)");
+    if ((e = hipMemsetAsync(h->fsync, 0, sizeof(sl::FusedSync), s)) != hipSuccess)
+      return cleanup_fail(e, "hipMemsetAsync(sync)");
+    if ((e = hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+      return cleanup_fail(e, "hipDeviceGetAttribute(compute units)");
 
     if (max_batch > 1 && w_dtype == SL_BF16) {
       h->upart_len = (int64_t)max_union_splits(n) * max_batch * m;
@@ -348,12 +354,21 @@ static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl
   // clears it, or a fill kernel does when no gate kernel runs. A product stage
   // run on its own adds onto y as it stands.
   const bool zero = plan.atomic && plan.splits > 1;
+  const size_t xsz = (h->wdt == SL_BF16) ? 2 : 4;
+  if (full && gate_wanted && h->fused && sl::fused_supported(h, x)) {
+    // gate and product of each token in one launch
+    for (int b = 0; b < B; ++b)
+      SL_HIP(sl::launch_fused(h, (const char*)x + (size_t)b * h->n * xsz, h->gout + b,
+                              mask_out ? mask_out + (size_t)b * h->n : nullptr, count_out ? count_out + b : nullptr,
+                              thresh_out ? thresh_out + b : nullptr, (char*)y + (size_t)b * h->m * ysz, y_dtype,
+                              plan.atomic, s));
+    return SL_OK;
+  }
   if (gate_wanted)
     SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, (zero && full) ? (float*)y : nullptr, s));
   else if (zero && full)
     SL_HIP(sl::launch_zero((float*)y, (int64_t)B * h->m, s));
   if (stages & SL_STAGE_PRODUCT) {
-    const size_t xsz = (h->wdt == SL_BF16) ? 2 : 4;
     for (int b = 0; b < B; ++b)
       SL_HIP(sl::launch_product(h, plan, (const char*)x + (size_t)b * h->n * xsz, h->gout + b, dense,
                                 (char*)y + (size_t)b * h->m * ysz, y_dtype, s));
@@ -410,6 +425,27 @@ sl_status sparse_linear_set_union_plan(sl_handle h, int32_t rows_per_tile, int32
   h->uplan_rows = rows_per_tile;
   h->uplan_wgs = workgroups;
   return SL_OK;
+}
+
+sl_status sparse_linear_set_fused(sl_handle h, int32_t on) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  h->fused = (on != 0);
+  return SL_OK;
+}
+
+sl_status sparse_linear_sync_status(sl_handle h, void* stream) {
+  if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+  sl_status st = check_device(h);
+  if (st != SL_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  SL_HIP(hipStreamSynchronize(s));
+  uint32_t err = 0;
+  SL_HIP(hipMemcpy(&err, &h->fsync->err, sizeof(err), hipMemcpyDeviceToHost));
+  if (err == 0) return SL_OK;
+  const uint32_t zero = 0;
+  SL_HIP(hipMemcpy(&h->fsync->err, &zero, sizeof(zero), hipMemcpyHostToDevice));
+  return fail(SL_ERR_HIP, "fused forward: a %s wait timed out (results of that forward are incomplete)",
+              err == 1 ? "product workgroup's gate" : "gate workgroup's acknowledgement");
 }
 
 sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on) {

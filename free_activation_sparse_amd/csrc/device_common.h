@@ -25,6 +25,12 @@ __device__ __forceinline__ bool gate_keep(uint32_t key, int j, uint32_t kthr, in
   return key > kthr || (key == kthr && j <= jlast);
 }
 
+// Index of this thread's wavefront in its workgroup, as a wavefront-uniform
+// (scalar) value: branches on it are then plain scalar branches. Left as
+// threadIdx.x / 64 the compiler treats them as lane-divergent and may place
+// register copies in exec-masked code that the other wavefronts skip.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // Number of lanes below this one whose bit is set in a wave-wide ballot.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t bal) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),

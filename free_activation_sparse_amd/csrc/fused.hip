@@ -1,0 +1,226 @@
+// Fused single-token forward: the gate and the index-list product in one
+// launch of 1024-thread workgroups.
+//
+//   workgroup 0      the gate (gate_body.h) for the token: scores, top-K or
+//                    statistical threshold, the optional mask / count /
+//                    threshold outputs; with the atomic split reduction it
+//                    also clears y (device-coherent stores issued right after
+//                    its input loads). It then publishes the kept-set pair
+//                    (kthr, jlast) in one 64-bit device-coherent flag word,
+//                    waits until every product workgroup has acknowledged it
+//                    and clears the flag and the acknowledgement counters for
+//                    the next launch.
+//   workgroups 1..P  one (row tile, input chunk) each of the product
+//                    (product_body.h): they load x and c of their chunk and
+//                    score it while the gate runs, wait for the flag (bounded
+//                    spin), then compact, stream the kept columns and reduce.
+//
+// One launch instead of two saves a kernel boundary per token and overlaps the
+// product's chunk loads with the gate. Progress: workgroups are dispatched in
+// index order on each XCD, so workgroup 0 holds a CU before any product
+// workgroup exists; every spin is bounded, and a timeout is recorded in the
+// error word (read by sparse_linear_sync_status) instead of hanging.
+#include "gate_body.h"
+#include "product_body.h"
+
+#include <algorithm>
+
+namespace {
+
+using namespace sl::dev;
+
+constexpr int FT = sl::gatedev::GT;  // threads per workgroup (16 wavefronts)
+constexpr uint32_t kSpinLimit = 1u << 20;  // polls (>= 50 ns each) before giving up
+
+struct GateSmem {
+  alignas(16) uint32_t h1[4096];
+  uint32_t h2[4096];
+  uint32_t h3[128];
+  uint64_t cand[64];
+  uint32_t wsum[FT / 64];
+  uint32_t res[4];
+  sl::gatedev::dd dsum[FT / 64][2];
+  uint32_t kminmax[FT / 64][2];
+};
+
+template <typename WT>
+struct ProdSmem {
+  int2 list[sl::kMaxChunk];
+  uint32_t wcnt[sl::kMaxChunk / 64 + 1];
+  float red[sl::proddev::red_floats<WT, FT>()];
+  uint32_t s_last;
+  uint64_t s_gate;
+};
+
+// (kthr, jlast) in one word that is never 0 (jlast >= -1).
+__device__ __forceinline__ uint64_t pack_gate(uint32_t kthr, int jlast) {
+  return ((uint64_t)(uint32_t)(jlast + 2) << 32) | (uint64_t)kthr;
+}
+
+template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC>
+__global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, const WT* __restrict__ x,
+                                                   const float* __restrict__ c, int m, int n, int K, double z,
+                                                   sl::GateOut* __restrict__ gout, uint8_t* __restrict__ mask_out,
+                                                   int32_t* __restrict__ count_out, double* __restrict__ thresh_out,
+                                                   int tiles, int splits, int chunk, float* __restrict__ partials,
+                                                   uint32_t* __restrict__ ctr, sl::FusedSync* __restrict__ sync,
+                                                   YT* __restrict__ y) {
+  __shared__ union {
+    GateSmem g;
+    ProdSmem<WT> p;
+  } sm;
+  const int t = threadIdx.x;
+  const int nprod = tiles * splits;
+
+  if (blockIdx.x == 0) {
+    uint32_t kthr;
+    int jlast;
+    float* zy = (ATOMIC && splits > 1) ? (float*)y : nullptr;
+    sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, 0.0f, gout, mask_out, count_out, thresh_out, zy, m,
+                                              sm.g.h1, sm.g.h2, sm.g.h3, sm.g.wsum, sm.g.res, sm.g.cand,
+                                              sm.g.dsum, sm.g.kminmax, 0, kthr, jlast);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
+    __syncthreads();
+    if (t == 0) __hip_atomic_store(&sync->flag, pack_gate(kthr, jlast), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < 64) {
+      // wavefront 0 sums the acknowledgement slots until every product
+      // workgroup has read the flag, then re-arms the hand-off
+      const int slot = t < sl::kAckSlots ? t : 0;
+      uint32_t it = 0, total = 0;
+      for (;;) {
+        const uint32_t a = t < sl::kAckSlots
+                               ? __hip_atomic_load(&sync->ack[16 * slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                               : 0u;
+        total = wave_sum(a);
+        if (total >= (uint32_t)nprod || ++it >= kSpinLimit) break;
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (t == 0 && total < (uint32_t)nprod)
+        __hip_atomic_store(&sync->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < sl::kAckSlots) __hip_atomic_store(&sync->ack[16 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == 0) __hip_atomic_store(&sync->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return;
+  }
+
+  const int pw = blockIdx.x - 1;
+  const int tile = pw % tiles;
+  const int split = pw / tiles;
+  const int j0 = split * chunk;
+  const int j1 = min(j0 + chunk, n);
+  sl::proddev::Chunk<FT> ch;
+  sl::proddev::load_chunk<WT, FT, false>(x, c, j0, j1, ch);
+  if (t == 0) {
+    uint64_t v = 0ull;
+    for (uint32_t it = 0; it < kSpinLimit; ++it) {
+      v = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (v != 0ull) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (v == 0ull) __hip_atomic_store(&sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm.p.s_gate = v;
+  }
+  __syncthreads();
+  const uint64_t v = sm.p.s_gate;
+  if (v == 0ull) {  // timed out: recorded in the error word
+    if (t == 0)
+      __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const uint32_t kthr = (uint32_t)v;
+  const int jlast = (int)(uint32_t)(v >> 32) - 2;
+  const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, kthr, jlast, sm.p.list, sm.p.wcnt);
+  // acknowledged after the chunk's loads have been consumed, so that waiting
+  // for the atomic overlaps the first weight loads instead of delaying them
+  if (t == 0)
+    __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  sl::proddev::stream_reduce<WT, YT, LPC, 8, FT, ATOMIC>(Wt, m, tile, split, splits, sm.p.list, cnt, sm.p.red,
+                                                         partials, ctr, &sm.p.s_last, y);
+}
+
+struct FusedPlan {
+  int tiles, splits, chunk;
+};
+
+// Row tiles of LPC * 8 rows; the input chunks are sized so that the product
+// workgroups fill the device's remaining workgroup slots once (chunks of
+// 32..kMaxChunk inputs), unless a split count is forced on the handle.
+FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu) {
+  FusedPlan p;
+  const int64_t n = h->n;
+  const int rows = lpc * 8;
+  p.tiles = (int)((h->m + rows - 1) / rows);
+  const int64_t slots = (int64_t)std::max(1, h->cus) * per_cu;
+  int64_t splits = h->plan_splits > 0 ? h->plan_splits : std::max<int64_t>(1, (slots - 1) / p.tiles);
+  splits = std::min<int64_t>(splits, std::min<int64_t>(sl::kMaxSplits, (n + 31) / 32));
+  splits = std::max<int64_t>(splits, (n + sl::kMaxChunk - 1) / sl::kMaxChunk);
+  p.chunk = (int)((n + splits - 1) / splits);
+  p.splits = (int)((n + p.chunk - 1) / p.chunk);
+  return p;
+}
+
+template <typename YT, int G, int MODE, int LPC, bool ATOMIC>
+hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt, double* th, void* y,
+              hipStream_t s) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC>, FT, 0) !=
+        hipSuccess)
+      nb = 1;
+    return std::max(1, nb);
+  }();
+  const FusedPlan p = plan_fused(h, LPC, per_cu);
+  fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(
+      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, (int)h->m, (int)h->n, (int)h->K, h->z, g, mask, cnt,
+      th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, (YT*)y);
+  return hipGetLastError();
+}
+
+template <typename YT, int G, int MODE, bool ATOMIC>
+hipError_t go_lpc(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt,
+                  double* th, void* y, hipStream_t s) {
+  int lpc = h->plan_rows > 0 ? h->plan_rows / 8 : (h->m >= 8192 ? 64 : (h->m >= 2048 ? 32 : 16));
+  switch (lpc) {
+    case 16: return go<YT, G, MODE, 16, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+    case 32: return go<YT, G, MODE, 32, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+    default: return go<YT, G, MODE, 64, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  }
+}
+
+template <typename YT, int G, bool ATOMIC>
+hipError_t go_mode(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt,
+                   double* th, void* y, hipStream_t s) {
+  if (h->gate == SL_GATE_STAT)
+    return go_lpc<YT, G, sl::gatedev::MODE_STAT, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  return go_lpc<YT, G, sl::gatedev::MODE_TOPK, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+}
+
+template <typename YT, bool ATOMIC>
+hipError_t go_g(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt,
+                double* th, void* y, hipStream_t s) {
+  const int64_t groups = (h->n + 4 * FT - 1) / (4 * FT);  // 1..8 for n <= 32768
+  if (groups <= 2) return go_mode<YT, 2, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  if (groups <= 3) return go_mode<YT, 3, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  if (groups <= 4) return go_mode<YT, 4, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  if (groups <= 5) return go_mode<YT, 5, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  if (groups <= 6) return go_mode<YT, 6, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  return go_mode<YT, 8, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+}
+
+}  // namespace
+
+namespace sl {
+
+bool fused_supported(const sl_linear* h, const void* x) {
+  return h->wdt == SL_BF16 && (h->gate == SL_GATE_TOPK || h->gate == SL_GATE_STAT) && h->n % 4 == 0 &&
+         ((uintptr_t)x % 8) == 0;
+}
+
+hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
+                        double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s) {
+  if (ydt == SL_BF16) return go_g<uint16_t, false>(h, x, g, mask_out, count_out, thresh_out, y, s);
+  if (atomic) return go_g<float, true>(h, x, g, mask_out, count_out, thresh_out, y, s);
+  return go_g<float, false>(h, x, g, mask_out, count_out, thresh_out, y, s);
+}
+
+}  // namespace sl

@@ -52,6 +52,19 @@ struct UnionPlan {
   bool atomic; // fp32 atomic split reduction (else ordered, reproducible)
 };
 
+// Hand-off from the gate workgroup to the product workgroups of one fused
+// launch (device memory, zero between launches). Acknowledgements are spread
+// over kAckSlots counters on separate 64-byte lines, so that the product
+// workgroups' atomic increments do not queue on one address.
+constexpr int kAckSlots = 64;
+struct FusedSync {
+  uint64_t flag;  // 0, or the kept-set pair: kthr | (jlast + 2) << 32
+  uint32_t err;   // nonzero after a timed-out wait (1: product side, 2: gate side)
+  uint32_t pad[13];
+  uint32_t ack[kAckSlots * 16];  // slot i at ack[16 * i]: product workgroups pw = i mod kAckSlots
+};
+static_assert(sizeof(FusedSync) == 64 + 64 * kAckSlots, "FusedSync layout");
+
 }  // namespace sl
 
 struct sl_linear {
@@ -74,10 +87,13 @@ struct sl_linear {
   float* upartials = nullptr;   // [usplits][max_batch][m] (union product)
   int64_t upart_len = 0;
   uint32_t* uctr = nullptr;     // [utiles]
+  sl::FusedSync* fsync = nullptr;  // fused gate + product hand-off
+  int cus = 0;                     // compute units of the device
 
   int plan_rows = 0, plan_splits = 0;  // overrides (0 = automatic)
   int uplan_rows = 0, uplan_wgs = 0;   // union-product overrides (0 = automatic)
   bool deterministic = false;          // ordered split reduction for fp32 y too
+  bool fused = true;                   // single-token forwards in one launch
 
 };
 
@@ -91,6 +107,11 @@ hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_o
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
                           void* y, sl_dtype ydt, hipStream_t s);
+// Fused gate + product for one token (bf16 weights, top-K or statistical
+// gate, n % 4 == 0 and x 8-byte aligned: fused_supported).
+bool fused_supported(const sl_linear* h, const void* x);
+hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
+                        double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,
                                 bool dense, void* y, sl_dtype ydt, hipStream_t s);
 

@@ -1,0 +1,240 @@
+// Phases of the single-token index-list product, shared by the product kernel
+// (256-thread workgroups) and the fused gate + product kernel (1024-thread
+// workgroups). PT is the workgroup size.
+//
+// This is the index-list product of the Spark Transformer article (section
+// 3.1): only the weight vectors of active inputs are read. W is column-major,
+// so each kept input contributes one contiguous run of m weights. A workgroup
+// owns one row tile and one chunk of inputs:
+//   1. load_chunk: x and c of the chunk (all loads in flight together) and
+//      the scores' keys;
+//   2. compact_chunk: the gate predicate on each input and a ballot
+//      compaction of the kept ones into LDS, ascending (no global index list);
+//   3. stream_reduce: the kept columns' row-tile runs with 16-byte
+//      non-temporal loads (each lane group owns every CS-th kept column and
+//      issues up to U loads before consuming any), fp32 accumulation, a fixed
+//      order reduction of the column slots in LDS, and the split reduction:
+//        ATOMIC    fp32 atomic adds into y (which must start at zero); one
+//                  memory round trip, summation order varies;
+//        otherwise device-coherent partial stores, then the last workgroup of
+//                  the tile to arrive (device-scope arrival counter) adds the
+//                  partials in a fixed order: reproducible to the bit, and the
+//                  path for bf16 outputs.
+#pragma once
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace sl {
+namespace proddev {
+
+using namespace sl::dev;
+
+// Thread t's share of a chunk: inputs j0 + q * PT + t.
+template <int PT>
+struct Chunk {
+  static constexpr int ROUNDS = sl::kMaxChunk / PT;
+  float xv[ROUNDS];
+  uint32_t kv[ROUNDS];
+};
+
+// Loads are unconditional (index clamped into the chunk) so that all of them
+// are in flight together; keys of a dense product are not needed.
+template <typename WT, int PT, bool DENSE>
+__device__ __forceinline__ void load_chunk(const WT* __restrict__ x, const float* __restrict__ c, int j0, int j1,
+                                           Chunk<PT>& ch) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < Chunk<PT>::ROUNDS; ++q) {
+    const int j = j0 + q * PT + t;
+    const int jc = j < j1 ? j : j1 - 1;
+    ch.xv[q] = load_elem(x + jc);
+    ch.kv[q] = DENSE ? 0u : score_key(ch.xv[q], c[jc]);
+  }
+}
+
+// Kept inputs of [j0, j1) as (j, x_j bits) pairs in list[0 .. count), in
+// ascending order. wcnt holds ROUNDS * PT / 64 + 1 words. Ends with a barrier.
+template <int PT, bool DENSE>
+__device__ __forceinline__ int compact_chunk(const Chunk<PT>& ch, int j0, int j1, uint32_t kthr, int jlast,
+                                             int2* list, uint32_t* wcnt) {
+  constexpr int ROUNDS = Chunk<PT>::ROUNDS;
+  constexpr int NW = PT / 64;
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int nr = (j1 - j0 + PT - 1) / PT;
+  uint64_t bal[ROUNDS];
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    const int j = j0 + q * PT + t;
+    const bool keep = q < nr && j < j1 && (DENSE || gate_keep(ch.kv[q], j, kthr, jlast));
+    bal[q] = __ballot(keep);
+    if (lane == 0) wcnt[q * NW + w] = (uint32_t)__popcll(bal[q]);
+  }
+  __syncthreads();
+  // wavefront 0 turns the ROUNDS * NW wavefront counts (round-major) into
+  // exclusive offsets in place; the total goes to wcnt[ROUNDS * NW]
+  static_assert(ROUNDS * NW <= 64, "one wavefront scans the counts");
+  if (w == 0) {
+    const uint32_t v = lane < ROUNDS * NW ? wcnt[lane] : 0u;
+    const uint32_t incl = wave_incl_scan(v);
+    if (lane < ROUNDS * NW) wcnt[lane] = incl - v;
+    if (lane == 63) wcnt[ROUNDS * NW] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < ROUNDS; ++q) {
+    if ((bal[q] >> lane) & 1ull)
+      list[wcnt[q * NW + w] + lanes_below(bal[q])] = make_int2(j0 + q * PT + t, __float_as_int(ch.xv[q]));
+  }
+  const int cnt = (int)wcnt[ROUNDS * NW];
+  __syncthreads();
+  return cnt;
+}
+
+// LDS floats stream_reduce needs in red: one VEC-wide accumulator per thread.
+template <typename WT, int PT>
+constexpr int red_floats() {
+  return PT * (16 / (int)sizeof(WT));
+}
+
+template <typename WT, typename YT, int LPC, int U, int PT, bool ATOMIC>
+__device__ __forceinline__ void stream_reduce(const WT* __restrict__ Wt, int m, int tile, int split, int splits,
+                                              const int2* list, int cnt, float* red, float* __restrict__ partials,
+                                              uint32_t* __restrict__ ctr, uint32_t* s_last, YT* __restrict__ y) {
+  constexpr int VEC = 16 / (int)sizeof(WT);  // elements per 16-byte run
+  constexpr int R = LPC * VEC;               // rows per tile
+  constexpr int CPW = 64 / LPC;              // column slots per wavefront
+  constexpr int CS = (PT / 64) * CPW;        // column slots per workgroup
+  static_assert(CS * R == red_floats<WT, PT>(), "slot buffer size");
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+
+  const int slot = w * CPW + lane / LPC;
+  const int sub = lane % LPC;
+  const int row = tile * R + sub * VEC;
+  float acc[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
+  if (row < m) {
+    const WT* base = Wt + row;
+    for (int k0 = slot; k0 < cnt; k0 += CS * U) {
+      int2 e[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int k = k0 + u * CS;
+        e[u] = list[k < cnt ? k : k0];
+      }
+      u32x4 wv[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (k0 + u * CS < cnt)
+          wv[u] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)e[u].x * (size_t)m));
+        else
+          wv[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) fma_run(acc, wv[u], k0 + u * CS < cnt ? __int_as_float(e[u].y) : 0.f);
+    }
+  }
+
+  // column slots in a fixed order
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) red[slot * R + sub * VEC + v] = acc[v];
+  __syncthreads();
+  constexpr int RQ = (R + PT - 1) / PT;
+  float part[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const int r = t + q * PT;
+    float s = 0.f;
+    if (r < R) {
+#pragma unroll
+      for (int k = 0; k < CS; ++k) s += red[k * R + r];
+    }
+    part[q] = s;
+  }
+
+  if (splits == 1) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int r = t + q * PT;
+      const int gr = tile * R + r;
+      if (r < R && gr < m) store_out(y + gr, part[q]);
+    }
+    return;
+  }
+
+  if constexpr (ATOMIC) {
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int r = t + q * PT;
+      const int gr = tile * R + r;
+      if (r < R && gr < m) atomicAdd((float*)(y + gr), part[q]);
+    }
+    return;
+  } else {
+    // Ordered reduction without cache-wide fences: partial sums are written with
+    // device-coherent stores, each workgroup waits for its stores to complete
+    // before it bumps the tile's arrival counter, and the last arrival reads the
+    // partials with device-coherent loads.
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int r = t + q * PT;
+      const int gr = tile * R + r;
+      if (r < R && gr < m)
+        __hip_atomic_store(partials + (size_t)split * m + gr, part[q], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (t == 0)
+      *s_last = (__hip_atomic_fetch_add(&ctr[tile], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(splits - 1))
+                    ? 1u
+                    : 0u;
+    __syncthreads();
+    if (*s_last == 0u) return;
+    // Thread t sums, for row (t mod RW), the splits g, g+G, g+2G, ... with
+    // g = t / RW (G groups), eight loads in flight at a time; the G group sums
+    // are then added in group order.
+    constexpr int RW = R < PT ? R : PT;
+    constexpr int G = PT / RW;
+    float* gsum = red;  // reuse: [G][R]
+#pragma unroll
+    for (int q = 0; q < RQ; ++q) {
+      const int r = (t % RW) + q * RW;
+      const int g = t / RW;
+      const int gr = tile * R + r;
+      float sacc = 0.f;
+      if (r < R && gr < m) {
+        const float* pp = partials + gr;
+        int k = g;
+        for (; k + 7 * G < splits; k += 8 * G) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u)
+            v[u] = __hip_atomic_load(pp + (size_t)(k + u * G) * m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) sacc += v[u];
+        }
+        for (; k < splits; k += G)
+          sacc += __hip_atomic_load(pp + (size_t)k * m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (G > 1) {
+        gsum[g * R + r] = sacc;
+        __syncthreads();
+        if (g == 0 && r < R && gr < m) {
+          float tot = 0.f;
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) tot += gsum[hh * R + r];
+          store_out(y + gr, tot);
+        }
+      } else if (r < R && gr < m) {
+        store_out(y + gr, sacc);
+      }
+    }
+    if (t == 0) __hip_atomic_store(&ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+}  // namespace proddev
+}  // namespace sl

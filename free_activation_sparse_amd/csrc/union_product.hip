@@ -15,11 +15,20 @@
 //      writes the zero-filled X_U tile to LDS (k-contiguous per token);
 //   2. walks the union in steps of 32 columns: the step's W tile (32 columns
 //      of R contiguous rows, 16-byte loads) goes to LDS in column order with a
-//      padded pitch, and MFMA operands are read back transposed (one row, eight
-//      consecutive union columns per lane) free of bank conflicts; the loads
-//      of the next D steps are in flight while the current one is multiplied;
-//   3. adds its [R][B] partial into Y: fp32 atomics, or the ordered
+//      padded pitch, and the MFMA A operand (one row, eight union columns per
+//      lane) is read back with two transposing LDS reads (ds_read_b64_tr_b16)
+//      free of bank conflicts; the loads of the next D steps are in flight
+//      while the current one is multiplied;
+//   3. stages its [R][B] partial through LDS so that every wavefront adds 64
+//      consecutive rows of one token into Y: fp32 atomics, or the ordered
 //      last-arrival reduction (bit-reproducible; bf16 outputs).
+//
+// Union column order inside a step. The contraction may take the 32 columns
+// of a step in any order as long as A and B agree. Lane l (group G = l / 16)
+// holds, as its eight k elements, the columns 4G + q (q = 0..3) and then
+// 16 + 4G + q: each half is one transposing read of four consecutive columns
+// per 16-lane group, and for the B operand one 8-byte read of X_U, which is
+// stored k-contiguous per token.
 #include "device_common.h"
 #include "internal.h"
 
@@ -28,13 +37,24 @@ namespace {
 using namespace sl::dev;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int UT = 256;             // threads per workgroup (4 wavefronts)
 constexpr int UK = 32;              // union columns per step (one MFMA k-depth)
-constexpr int XPITCH = 2 * sl::kUnionMaxChunk + 16;  // bytes per token row of X_U
+// bytes per token row of X_U: 16 mod 256, so the 16 tokens of an 8-byte
+// operand read fall on disjoint banks
+constexpr int XPITCH = 2 * sl::kUnionMaxChunk + 16;
 
-__device__ __forceinline__ uint16_t lds_u16(const uint8_t* p) { return *(const uint16_t*)p; }
+// Transposing LDS read: within each 16-lane group, lane i supplies the address
+// of four consecutive bf16; lane l receives element (l mod 4) of the rows that
+// lanes 4q + (l mod 16) / 4 addressed, q = 0..3.
+__device__ __forceinline__ i16x4 lds_read_tr(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+__device__ __forceinline__ i16x4 lds_read_b64(const uint8_t* p) { return *(const i16x4*)p; }
 
 // NB: 16-row MFMA blocks per wavefront (tile of R = 64 * NB rows); D: column
 // steps whose loads are in flight ahead of the one being multiplied.
@@ -46,12 +66,16 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
                                                    float* __restrict__ partials, uint32_t* __restrict__ ctr,
                                                    YT* __restrict__ y) {
   constexpr int UR = 64 * NB;          // rows per tile
-  // bytes per staged column: R/2 + 1 dwords (1 mod 4), so the four 8-column
-  // groups of a transposed operand read land on disjoint LDS banks
-  constexpr int WPITCH = 2 * UR + 4;
+  // bytes per staged column: 2R + 32 (32 mod 256), so the eight 32-byte
+  // column pieces that 32 lanes of a transposing read address fall on
+  // disjoint LDS banks; a multiple of 16 keeps the tile stores 16-byte wide
+  constexpr int WPITCH = 2 * UR + 32;
+  // fp32 [token][row] staging of the partial in phase 3 (reuses ws)
+  constexpr int OPITCH = 4 * UR + 16;
+  static_assert(16 * OPITCH <= 2 * UK * WPITCH, "partial staging must fit the W buffers");
   __shared__ __align__(16) uint8_t ws[2][UK * WPITCH];     // staged W tiles, column-major
   __shared__ __align__(16) uint8_t xu[16 * XPITCH];        // X_U, [token][k] bf16
-  __shared__ int ulist[sl::kUnionMaxChunk + UK];           // union column indices
+  __shared__ uint16_t ulist[sl::kUnionMaxChunk + UK];      // union columns, offsets from j0
   __shared__ uint32_t wcnt[sl::kUnionMaxChunk / UT][4];
   __shared__ uint32_t gk[16];
   __shared__ int gj[16];
@@ -59,7 +83,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
 
   const int tile = blockIdx.x % tiles;
   const int split = blockIdx.x / tiles;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const int j0 = split * chunk;
   const int j1 = min(j0 + chunk, n);
   const int row0 = tile * UR;
@@ -110,7 +134,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
       for (int k = 0; k < w; ++k) off += wcnt[q][k];
       if (tmask[q] != 0u) {
         const int pos = (int)(off + lanes_below(bal[q]));
-        ulist[pos] = j0 + q * UT + t;
+        ulist[pos] = (uint16_t)(q * UT + t);
 #pragma unroll
         for (int b = 0; b < 16; ++b)
           *(uint16_t*)(xu + b * XPITCH + 2 * pos) = ((tmask[q] >> b) & 1u) ? xr[q][b] : (uint16_t)0;
@@ -121,7 +145,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   // pad the union to a multiple of UK: column j0 (any valid one) with zero inputs
   const int cntp = (cnt + UK - 1) / UK * UK;
   for (int k = cnt + t; k < cntp; k += UT) {
-    ulist[k] = j0;
+    ulist[k] = 0;
     for (int b = 0; b < 16; ++b) *(uint16_t*)(xu + b * XPITCH + 2 * k) = 0;
   }
   __syncthreads();
@@ -138,14 +162,17 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
     lcol[i] = v / VPC;
     lrow[i] = (v % VPC) * 8;
     // clamped into range; rows >= m are loaded from row m - 8 and never written
-    gsrc[i] = Wt + min(row0 + lrow[i], m - 8);
+    gsrc[i] = Wt + (size_t)j0 * m + min(row0 + lrow[i], m - 8);
   }
   f32x4 acc[NB];
 #pragma unroll
   for (int h = 0; h < NB; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int rb = w * 16 * NB;  // this wavefront's rows inside the tile
   const int ti = lane & 15;    // token (B operand column) / row within block
-  const int kg = lane >> 4;    // k group of 8
+  const int kg = lane >> 4;    // k group (G)
+  // transposing-read address of this lane: column 4G + ti/4 (+16 for the
+  // second half), rows rb + 4 (ti mod 4) .. +4 (+16 per block h)
+  const int aoff = (4 * kg + (ti >> 2)) * WPITCH + 2 * (rb + 4 * (ti & 3));
   const int nsteps = cntp / UK;
   u32x4 pr[D][NB];             // ring of prefetched steps: step q lives in slot q % D
   auto gload = [&](int slot, int q) {
@@ -158,9 +185,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   auto lstore = [&](int slot, int buf) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      uint32_t* d = (uint32_t*)(ws[buf] + lcol[i] * WPITCH + 2 * lrow[i]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = pr[slot][i][q];
+      *(u32x4*)(ws[buf] + lcol[i] * WPITCH + 2 * lrow[i]) = pr[slot][i];
     }
   };
 #pragma unroll
@@ -174,16 +199,17 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
     for (int u = 0; u < D; ++u) {
       const int s = s0 + u;  // s % D == u
       if (s < nsteps) {
-        // B operand: X_U[k = 8*kg .. +8][token ti]
-        const bf16x8 bop = *(const bf16x8*)(xu + ti * XPITCH + 2 * (s * UK + 8 * kg));
-        const uint8_t* wb = ws[s & 1];
+        // B operand: X_U[the lane's eight step columns][token ti]
+        const uint8_t* xb = xu + ti * XPITCH + 2 * (s * UK + 4 * kg);
+        const bf16x8 bop = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(lds_read_b64(xb), lds_read_b64(xb + 32), 0, 1, 2, 3, 4, 5, 6, 7));
+        const uint8_t* wb = ws[s & 1] + aoff;
 #pragma unroll
         for (int h = 0; h < NB; ++h) {
-          // A operand: W[row rb + 16h + ti][k = 8*kg + q]
-          bf16x8 a;
-#pragma unroll
-          for (int q = 0; q < 8; ++q)
-            a[q] = __builtin_bit_cast(__bf16, lds_u16(wb + (8 * kg + q) * WPITCH + 2 * (rb + 16 * h + ti)));
+          // A operand: W[row rb + 16h + ti][the same eight columns]
+          const i16x4 lo = lds_read_tr(wb + 32 * h);
+          const i16x4 hi = lds_read_tr(wb + 16 * WPITCH + 32 * h);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bop, acc[h], 0, 0, 0);
         }
         if (s + 1 < nsteps) lstore((u + 1) % D, (s + 1) & 1);
@@ -194,37 +220,29 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   }
 
   // 3. partial [rows][tokens] of this chunk into Y. Lane holds rows
-  //    rb + 16h + 4*kg + q for token ti.
-  const int tok = ti;
-  const bool tok_ok = tok < B;
-  if (splits == 1 || ATOMIC) {
+  //    rb + 16h + 4*kg + q for token ti; after the last step's barrier the W
+  //    buffers are free and take the partial as fp32 [token][row].
+  uint8_t* ob = &ws[0][0];
 #pragma unroll
-    for (int h = 0; h < NB; ++h) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = row0 + rb + 16 * h + 4 * kg + q;
-        if (tok_ok && row < m) {
-          if (splits == 1)
-            store_out(y + (size_t)tok * m + row, acc[h][q]);
-          else
-            atomicAdd((float*)(y + (size_t)tok * m + row), acc[h][q]);
-        }
-      }
-    }
-    return;
-  }
-  // ordered reduction: device-coherent partial stores [split][token][row], the
-  // last arrival of the tile adds them in split order
-#pragma unroll
-  for (int h = 0; h < NB; ++h) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int row = row0 + rb + 16 * h + 4 * kg + q;
-      if (tok_ok && row < m)
-        __hip_atomic_store(partials + ((size_t)split * B + tok) * m + row, acc[h][q], __ATOMIC_RELAXED,
+  for (int h = 0; h < NB; ++h) *(f32x4*)(ob + ti * OPITCH + 4 * (rb + 16 * h + 4 * kg)) = acc[h];
+  __syncthreads();
+  const bool ordered = !(splits == 1 || ATOMIC);
+  for (int e = t; e < UR * B; e += UT) {
+    const int tk = e / UR, r = e % UR, row = row0 + r;
+    if (row < m) {
+      const float v = *(const float*)(ob + tk * OPITCH + 4 * r);
+      if (splits == 1)
+        store_out(y + (size_t)tk * m + row, v);
+      else if (ATOMIC)
+        atomicAdd((float*)(y + (size_t)tk * m + row), v);
+      else
+        __hip_atomic_store(partials + ((size_t)split * B + tk) * m + row, v, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+  if (!ordered) return;
+  // ordered reduction: the device-coherent partial stores [split][token][row]
+  // above are complete; the last arrival of the tile adds them in split order
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (t == 0)

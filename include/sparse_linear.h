@@ -109,7 +109,10 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
  *
  * Each token's kept set depends only on that token. For B > 1 the library
  * forms the union of the B masks and runs one matrix-core pass over the union
- * columns, feeding zero for inputs a token did not keep.
+ * columns, feeding zero for inputs a token did not keep. A single bf16 token
+ * with a top-K or statistical gate (n % 4 == 0, x 8-byte aligned) runs as one
+ * fused launch: one workgroup selects while the others load their input
+ * chunks, then stream the kept columns (see sparse_linear_set_fused).
  * Asynchronous on `stream`; the caller keeps x, y and the optional outputs
  * alive until the stream has completed. A handle's scratch is shared by its
  * calls, so one handle must not run on two streams at once.
@@ -172,9 +175,26 @@ sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, vo
 sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on);
 
 /*
+ * Fused single-token forward (on != 0, the default) or the two-launch form
+ * (gate kernel, then product kernel) for comparison. Both give the same
+ * selection and outputs within the split reduction's summation order.
+ */
+sl_status sparse_linear_set_fused(sl_handle h, int32_t on);
+
+/*
+ * Synchronize `stream` and report whether any fused forward of this handle
+ * since the last call had a hand-off wait time out (its gate workgroup not
+ * running within about a second, which in-order workgroup dispatch rules out
+ * on an otherwise working device). Returns SL_OK, or SL_ERR_HIP with
+ * sparse_linear_last_error describing the wait; the record is then cleared.
+ * Such a forward's y is incomplete.
+ */
+sl_status sparse_linear_sync_status(sl_handle h, void* stream);
+
+/*
  * Launch-shape override for tuning sweeps: rows_per_tile in {128, 256, 512}
  * (0 = automatic) and splits >= 0 (0 = automatic) for the single-token product
- * kernel. Takes effect on the next forward.
+ * kernel and the fused forward. Takes effect on the next forward.
  */
 sl_status sparse_linear_set_plan(sl_handle h, int32_t rows_per_tile, int32_t splits);
 

@@ -100,6 +100,10 @@ def test_forward_rejects_null_handle_and_pointers(slib):
     assert L.sparse_linear_get_norms(None, 1, None) == 1
     assert L.sparse_linear_destroy(None) == 0
     assert L.sparse_linear_set_plan(None, 0, 0) == 1
+    assert L.sparse_linear_set_union_plan(None, 0, 0) == 1
+    assert L.sparse_linear_set_deterministic(None, 1) == 1
+    assert L.sparse_linear_set_fused(None, 1) == 1
+    assert L.sparse_linear_sync_status(None, None) == 1
 
 
 def test_strerror(slib):

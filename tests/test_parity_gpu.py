@@ -32,7 +32,7 @@ def _layer(fas, W, c, mode, K=None, s_keep=None, tau=None, layout="rowmajor", ma
 
 def _fwd(layer, x, **kw):
     out = layer.forward(to_dev(x, torch)[None, :], mask=True, count=True, thresh=True, **kw)
-    torch.cuda.synchronize()
+    layer.sync_status()  # synchronizes; raises if a fused hand-off timed out
     return out
 
 
@@ -67,11 +67,13 @@ def llama_down():
     return W, oracle.column_norms(W)
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("sparsity", [0.5, 0.65])
-def test_llama7b_down_full_size(fas, llama_down, sparsity):
+def test_llama7b_down_full_size(fas, llama_down, sparsity, fused):
     W, c = llama_down
     K = wl.k_from_sparsity(W.shape[1], sparsity)
     layer = _layer(fas, W, c, "topk", K=K)
+    layer.set_fused(fused)
     rows = np.random.default_rng(7).choice(W.shape[0], 96, replace=False)
     for t in range(12):
         x = wl.token(2, 0, t)
@@ -132,8 +134,8 @@ EDGE_SHAPES = [(8, 1), (136, 1000), (520, 2049), (1032, 300), (64, 4100)]
 
 
 @pytest.mark.parametrize("m,n", EDGE_SHAPES)
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_ragged_shapes_topk(fas, m, n, dtype):
+@pytest.mark.parametrize("dtype,fused", [("bf16", True), ("bf16", False), ("f32", False)])
+def test_ragged_shapes_topk(fas, m, n, dtype, fused):
     W = wl.random_matrix(m * 7 + n, m, n, dtype)
     c = oracle.column_norms(W)
     g = np.random.default_rng(m + n)
@@ -141,9 +143,10 @@ def test_ragged_shapes_topk(fas, m, n, dtype):
         if K < 0:
             continue
         layer = _layer(fas, W, c, "topk", K=K)
+        layer.set_fused(fused)
         for t, kind in enumerate(["normal", "ties"]):
             x = wl.random_tokens(m + n + t, 1, n, dtype, kind)[0]
-            print(f"[ragged {dtype} {m}x{n}] K={K} {kind}", flush=True)
+            print(f"[ragged {dtype} {m}x{n} fused={fused}] K={K} {kind}", flush=True)
             check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, ctx=f"ragged {m}x{n} K={K} {kind}")
         layer.close()
     del g
@@ -198,10 +201,13 @@ def test_topk_all_equals_dense_kernel(fas):
     layer = _layer(fas, W, c, "topk", K=n)
     layer.set_deterministic(True)  # ordered reduction: same kernel, same bits
     x = to_dev(wl.random_tokens(11, 1, n, "bf16")[0], torch)[None, :]
+    yf = layer.forward(x)["y"].clone()  # fused launch: its own split plan
+    layer.set_fused(False)
     ys = layer.forward(x)["y"]
     yd = layer.forward_dense(x)
-    torch.cuda.synchronize()
+    layer.sync_status()
     assert torch.equal(ys, yd)
+    assert rel_l2(yf[0].cpu().numpy(), yd[0].cpu().numpy()) <= 1e-6
     ref = oracle.sparse_product(W, wl.random_tokens(11, 1, n, "bf16")[0], np.arange(n))
     assert rel_l2(yd[0].cpu().numpy(), ref) <= REL_L2_TOL
     layer.close()
@@ -307,19 +313,23 @@ def test_graph_replay_matches_eager(fas, llama_down):
         l.close()
 
 
+@pytest.mark.parametrize("fused", [True, False])
 @pytest.mark.parametrize("det", [False, True])
-def test_reduction_modes_match_oracle(fas, llama_down, det):
+def test_reduction_modes_match_oracle(fas, llama_down, det, fused):
     """Both split reductions (atomic fp32, ordered) and the bf16 output, at
-    several launch shapes, on the full Llama-7B down projection."""
+    several launch shapes, on the full Llama-7B down projection, for the fused
+    launch and the gate + product launches."""
     W, c = llama_down
     K = wl.k_from_sparsity(W.shape[1], 0.5)
     layer = _layer(fas, W, c, "topk", K=K)
     layer.set_deterministic(det)
+    layer.set_fused(fused)
     rows = np.arange(0, W.shape[0], 41)
     for rpt, splits in ((128, 16), (256, 32), (512, 0), (128, 1)):
         layer.set_plan(rpt, splits)
         for t in range(2):
             x = wl.token(2, 0, 40 + t)
+            print(f"[reduction det={det} fused={fused}] {rpt}/{splits} token {t}", flush=True)
             check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=rows, ctx=f"det={det} {rpt}/{splits}")
             check_token(_fwd(layer, x, y_dtype=torch.bfloat16), 0, W, c, x, "topk", K=K, rows=rows,
                         ctx=f"det={det} bf16 {rpt}/{splits}")
@@ -340,3 +350,60 @@ def test_dense_forward_modes(fas, llama_down):
         assert rel_l2(y[0].cpu().numpy(), ref) <= REL_L2_TOL
         assert rel_l2(yb[0].float().cpu().numpy(), ref) <= REL_L2_TOL
     layer.close()
+
+
+# ---------------------------------------------------------------- fused launch vs gate + product launches
+@pytest.mark.parametrize("mode", ["topk", "stat"])
+def test_fused_matches_two_launch(fas, mode):
+    """The fused launch and the gate kernel + product kernel give identical
+    masks, counts and thresholds, and the same y up to summation order, over
+    shapes that take every gate register variant (n up to 32768)."""
+    for m, n in ((256, 4096), (1024, 8200), (512, 16384), (256, 20480), (128, 32768)):
+        W = wl.random_matrix(90 + n, m, n, "bf16")
+        c = oracle.column_norms(W)
+        g = dict(K=n // 3) if mode == "topk" else dict(s_keep=0.1)
+        layer = _layer(fas, W, c, mode, **g)
+        x = wl.random_tokens(91 + n, 1, n, "bf16", "laplace")[0]
+        print(f"[fused vs two-launch {mode}] {m}x{n}", flush=True)
+        layer.set_fused(True)
+        a = _fwd(layer, x)
+        a = {k: v.clone() for k, v in a.items()}
+        layer.set_fused(False)
+        b = _fwd(layer, x)
+        assert torch.equal(a["mask"], b["mask"])
+        assert torch.equal(a["count"], b["count"])
+        assert torch.equal(a["thresh"], b["thresh"])
+        assert rel_l2(a["y"][0].cpu().numpy(), b["y"][0].cpu().numpy()) <= 1e-6
+        layer.set_fused(True)
+        check_token(a, 0, W, c, x, mode, rows=np.arange(0, m, 5), ctx=f"fused {m}x{n}", **g)
+        layer.close()
+
+
+def test_fused_graph_replays_rearm(fas):
+    """The fused launch re-arms its hand-off word itself: many captured
+    forwards of two layers, replayed repeatedly, give the eager results."""
+    m, n = 2048, 5120
+    W = wl.random_matrix(95, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layers = [_layer(fas, W, c, "topk", K=1500), _layer(fas, W, c, "stat", s_keep=0.2)]
+    for l in layers:
+        l.set_deterministic(True)
+    xs = [to_dev(wl.random_tokens(96 + t, 1, n, "bf16", "laplace")[0], torch)[None, :] for t in range(8)]
+    eager = [layers[i % 2].forward(x)["y"].clone() for i, x in enumerate(xs)]
+    ys = [torch.empty((1, m), dtype=torch.float32, device="cuda:0") for _ in xs]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i, (x, y) in enumerate(zip(xs, ys)):
+            layers[i % 2].forward(x, y=y)
+    for rep in range(5):
+        for y in ys:
+            y.fill_(float("nan"))
+        layers[1].forward(xs[rep])
+        torch.cuda.synchronize()
+        g.replay()
+        for l in layers:
+            l.sync_status()
+        for i, (y, e) in enumerate(zip(ys, eager)):
+            assert torch.equal(y, e), f"replay {rep} forward {i}"
+    for l in layers:
+        l.close()
