@@ -31,6 +31,7 @@ using namespace sl::dev;
 
 constexpr int FT = sl::gatedev::GT;  // threads per workgroup (16 wavefronts)
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls (>= 50 ns each) before giving up
+constexpr float kSpecMargin = 1.15f;       // speculation bound over the previous threshold score
 
 struct GateSmem {
   alignas(16) uint32_t h1[4096];
@@ -57,7 +58,10 @@ __device__ __forceinline__ uint64_t pack_gate(uint32_t kthr, int jlast) {
   return ((uint64_t)(uint32_t)(jlast + 2) << 32) | (uint64_t)kthr;
 }
 
-template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC>
+// SPEC (speculation) only with the atomic reduction, whose summation order
+// varies anyway: with the ordered reduction the result must not depend on
+// the previous call.
+template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC, bool SPEC = ATOMIC>
 __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, const WT* __restrict__ x,
                                                    const float* __restrict__ c, int m, int n, int K, double z,
                                                    sl::GateOut* __restrict__ gout, uint8_t* __restrict__ mask_out,
@@ -108,8 +112,28 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   const int split = pw / tiles;
   const int j0 = split * chunk;
   const int j1 = min(j0 + chunk, n);
+  // the handle's previous threshold key (any value read here is safe: it only
+  // steers the speculation below, which is checked against the exact pair)
+  const uint32_t prevk = SPEC ? __hip_atomic_load(&gout->kthr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
   sl::proddev::Chunk<FT> ch;
   sl::proddev::load_chunk<WT, FT, false>(x, c, j0, j1, ch);
+  sl::proddev::Acc<WT> acc;
+#pragma unroll
+  for (int v = 0; v < sl::proddev::Acc<WT>::VEC; ++v) acc.v[v] = 0.f;
+
+  // Speculation: while the gate runs, stream the inputs whose score is at
+  // least kSpecMargin times the previous threshold; consecutive tokens'
+  // thresholds differ by a few percent, so these are almost always kept.
+  uint32_t g0 = 0xffffffffu;  // no speculation
+  if (SPEC && prevk != 0u && prevk < 0x7f800000u) {
+    g0 = __float_as_uint(__uint_as_float(prevk) * kSpecMargin);
+    if (g0 <= prevk) g0 = prevk + 1u;
+  }
+  if (g0 != 0xffffffffu) {
+    const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, g0 - 1u, -1, sm.p.list, sm.p.wcnt);
+    sl::proddev::stream_accum<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt, acc);
+  }
+
   if (t == 0) {
     uint64_t v = 0ull;
     for (uint32_t it = 0; it < kSpinLimit; ++it) {
@@ -129,13 +153,22 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   }
   const uint32_t kthr = (uint32_t)v;
   const int jlast = (int)(uint32_t)(v >> 32) - 2;
-  const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, kthr, jlast, sm.p.list, sm.p.wcnt);
+  // every speculated input is kept iff the bound lies above the threshold
+  // key; otherwise the speculative sums are dropped and everything is redone
+  uint32_t below = g0;
+  if (g0 != 0xffffffffu && g0 <= kthr) {
+#pragma unroll
+    for (int q = 0; q < sl::proddev::Acc<WT>::VEC; ++q) acc.v[q] = 0.f;
+    below = 0xffffffffu;
+  }
+  const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, kthr, jlast, sm.p.list, sm.p.wcnt, below);
   // acknowledged after the chunk's loads have been consumed, so that waiting
-  // for the atomic overlaps the first weight loads instead of delaying them
+  // for the atomic overlaps the weight loads instead of delaying them
   if (t == 0)
     __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  sl::proddev::stream_reduce<WT, YT, LPC, 8, FT, ATOMIC>(Wt, m, tile, split, splits, sm.p.list, cnt, sm.p.red,
-                                                         partials, ctr, &sm.p.s_last, y);
+  sl::proddev::stream_accum<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt, acc);
+  sl::proddev::reduce_out<WT, YT, LPC, FT, ATOMIC>(acc, m, tile, split, splits, sm.p.red, partials, ctr,
+                                                   &sm.p.s_last, y);
 }
 
 struct FusedPlan {

@@ -53,11 +53,12 @@ __device__ __forceinline__ void load_chunk(const WT* __restrict__ x, const float
   }
 }
 
-// Kept inputs of [j0, j1) as (j, x_j bits) pairs in list[0 .. count), in
-// ascending order. wcnt holds ROUNDS * PT / 64 + 1 words. Ends with a barrier.
+// Kept inputs of [j0, j1) whose key is below `below`, as (j, x_j bits) pairs
+// in list[0 .. count), in ascending order. wcnt holds ROUNDS * PT / 64 + 1
+// words. Ends with a barrier.
 template <int PT, bool DENSE>
 __device__ __forceinline__ int compact_chunk(const Chunk<PT>& ch, int j0, int j1, uint32_t kthr, int jlast,
-                                             int2* list, uint32_t* wcnt) {
+                                             int2* list, uint32_t* wcnt, uint32_t below = 0xffffffffu) {
   constexpr int ROUNDS = Chunk<PT>::ROUNDS;
   constexpr int NW = PT / 64;
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
@@ -66,7 +67,7 @@ __device__ __forceinline__ int compact_chunk(const Chunk<PT>& ch, int j0, int j1
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * PT + t;
-    const bool keep = q < nr && j < j1 && (DENSE || gate_keep(ch.kv[q], j, kthr, jlast));
+    const bool keep = q < nr && j < j1 && (DENSE || (gate_keep(ch.kv[q], j, kthr, jlast) && ch.kv[q] < below));
     bal[q] = __ballot(keep);
     if (lane == 0) wcnt[q * NW + w] = (uint32_t)__popcll(bal[q]);
   }
@@ -97,44 +98,64 @@ constexpr int red_floats() {
   return PT * (16 / (int)sizeof(WT));
 }
 
-template <typename WT, typename YT, int LPC, int U, int PT, bool ATOMIC>
-__device__ __forceinline__ void stream_reduce(const WT* __restrict__ Wt, int m, int tile, int split, int splits,
-                                              const int2* list, int cnt, float* red, float* __restrict__ partials,
-                                              uint32_t* __restrict__ ctr, uint32_t* s_last, YT* __restrict__ y) {
-  constexpr int VEC = 16 / (int)sizeof(WT);  // elements per 16-byte run
+// Accumulator of one thread: rows tile * R + sub * VEC .. + VEC of its
+// column slot.
+template <typename WT>
+struct Acc {
+  static constexpr int VEC = 16 / (int)sizeof(WT);
+  float v[VEC];
+};
+
+// Streams the row-tile runs of list[0 .. cnt) into acc (added to what it
+// holds).
+template <typename WT, int LPC, int U, int PT>
+__device__ __forceinline__ void stream_accum(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
+                                             Acc<WT>& a) {
+  constexpr int VEC = Acc<WT>::VEC;          // elements per 16-byte run
   constexpr int R = LPC * VEC;               // rows per tile
   constexpr int CPW = 64 / LPC;              // column slots per wavefront
   constexpr int CS = (PT / 64) * CPW;        // column slots per workgroup
-  static_assert(CS * R == red_floats<WT, PT>(), "slot buffer size");
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
-
   const int slot = w * CPW + lane / LPC;
   const int sub = lane % LPC;
   const int row = tile * R + sub * VEC;
-  float acc[VEC];
+  if (row >= m) return;
+  const WT* base = Wt + row;
+  for (int k0 = slot; k0 < cnt; k0 += CS * U) {
+    int2 e[U];
 #pragma unroll
-  for (int v = 0; v < VEC; ++v) acc[v] = 0.f;
-  if (row < m) {
-    const WT* base = Wt + row;
-    for (int k0 = slot; k0 < cnt; k0 += CS * U) {
-      int2 e[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int k = k0 + u * CS;
-        e[u] = list[k < cnt ? k : k0];
-      }
-      u32x4 wv[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (k0 + u * CS < cnt)
-          wv[u] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)e[u].x * (size_t)m));
-        else
-          wv[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) fma_run(acc, wv[u], k0 + u * CS < cnt ? __int_as_float(e[u].y) : 0.f);
+    for (int u = 0; u < U; ++u) {
+      const int k = k0 + u * CS;
+      e[u] = list[k < cnt ? k : k0];
     }
+    u32x4 wv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k0 + u * CS < cnt)
+        wv[u] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)e[u].x * (size_t)m));
+      else
+        wv[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) fma_run(a.v, wv[u], k0 + u * CS < cnt ? __int_as_float(e[u].y) : 0.f);
   }
+}
+
+// Adds the workgroup's column slots in a fixed order and the split partial
+// into y (see the header comment for the two reductions).
+template <typename WT, typename YT, int LPC, int PT, bool ATOMIC>
+__device__ __forceinline__ void reduce_out(const Acc<WT>& a, int m, int tile, int split, int splits, float* red,
+                                           float* __restrict__ partials, uint32_t* __restrict__ ctr,
+                                           uint32_t* s_last, YT* __restrict__ y) {
+  constexpr int VEC = Acc<WT>::VEC;
+  constexpr int R = LPC * VEC;
+  constexpr int CPW = 64 / LPC;
+  constexpr int CS = (PT / 64) * CPW;
+  static_assert(CS * R == red_floats<WT, PT>(), "slot buffer size");
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  const int slot = w * CPW + lane / LPC;
+  const int sub = lane % LPC;
+  const float* acc = a.v;
 
   // column slots in a fixed order
 #pragma unroll
@@ -234,6 +255,17 @@ __device__ __forceinline__ void stream_reduce(const WT* __restrict__ Wt, int m, 
     }
     if (t == 0) __hip_atomic_store(&ctr[tile], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+template <typename WT, typename YT, int LPC, int U, int PT, bool ATOMIC>
+__device__ __forceinline__ void stream_reduce(const WT* __restrict__ Wt, int m, int tile, int split, int splits,
+                                              const int2* list, int cnt, float* red, float* __restrict__ partials,
+                                              uint32_t* __restrict__ ctr, uint32_t* s_last, YT* __restrict__ y) {
+  Acc<WT> a;
+#pragma unroll
+  for (int v = 0; v < Acc<WT>::VEC; ++v) a.v[v] = 0.f;
+  stream_accum<WT, LPC, U, PT>(Wt, m, tile, list, cnt, a);
+  reduce_out<WT, YT, LPC, PT, ATOMIC>(a, m, tile, split, splits, red, partials, ctr, s_last, y);
 }
 
 }  // namespace proddev

@@ -407,3 +407,30 @@ def test_fused_graph_replays_rearm(fas):
             assert torch.equal(y, e), f"replay {rep} forward {i}"
     for l in layers:
         l.close()
+
+
+def test_fused_speculation_paths(fas):
+    """The fused launch streams, ahead of its gate, the inputs whose score is
+    well above the handle's previous threshold, and checks that bound against
+    the exact threshold. Token scales jumping between calls make the
+    speculation fail (dropped and redone), hold, or be empty; every call must
+    still match the oracle exactly in mask, count and threshold."""
+    m, n = 1024, 6144
+    W = wl.random_matrix(120, m, n, "bf16")
+    c = oracle.column_norms(W)
+    base = [wl.bf16_bits_to_f32(wl.random_tokens(121 + i, 1, n, "bf16", "laplace")[0]) for i in range(4)]
+    scales = [1.0, 1.0, 0.1, 1.0, 10.0, 10.0, 1e-3, 1.0, 1.0, 1.05, 0.95]
+    for K in (1, 700, n // 2, n - 1, n):
+        layer = _layer(fas, W, c, "topk", K=K)
+        for i, sc in enumerate(scales):
+            x = wl.f32_to_bf16_bits(base[i % 4] * np.float32(sc))
+            print(f"[speculation] K={K} call {i} scale {sc}", flush=True)
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=np.arange(0, m, 3),
+                        ctx=f"speculation K={K} call {i}")
+        layer.close()
+    layer = _layer(fas, W, c, "stat", s_keep=0.2)
+    for i, sc in enumerate(scales):
+        x = wl.f32_to_bf16_bits(base[i % 4] * np.float32(sc))
+        check_token(_fwd(layer, x), 0, W, c, x, "stat", s_keep=0.2, rows=np.arange(0, m, 3),
+                    ctx=f"speculation stat call {i}")
+    layer.close()
