@@ -53,6 +53,10 @@ struct ProdSmem {
   uint64_t s_gate;
 };
 
+// (kthr, jlast) in one word that is never 0 (jlast >= -1) and never below
+// 2^32, so 1 can mark a wait that timed out.
+constexpr uint64_t kGateTimeout = 1ull;
+
 // (kthr, jlast) in one word that is never 0 (jlast >= -1).
 __device__ __forceinline__ uint64_t pack_gate(uint32_t kthr, int jlast) {
   return ((uint64_t)(uint32_t)(jlast + 2) << 32) | (uint64_t)kthr;
@@ -115,6 +119,7 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   // the handle's previous threshold key (any value read here is safe: it only
   // steers the speculation below, which is checked against the exact pair)
   const uint32_t prevk = SPEC ? __hip_atomic_load(&gout->kthr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  static_assert(sl::proddev::Chunk<FT>::ROUNDS == 1, "one input per thread");
   sl::proddev::Chunk<FT> ch;
   sl::proddev::load_chunk<WT, FT, false>(x, c, j0, j1, ch);
   sl::proddev::Acc<WT> acc;
@@ -129,44 +134,81 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
     g0 = __float_as_uint(__uint_as_float(prevk) * kSpecMargin);
     if (g0 <= prevk) g0 = prevk + 1u;
   }
-  if (g0 != 0xffffffffu) {
-    const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, g0 - 1u, -1, sm.p.list, sm.p.wcnt);
-    sl::proddev::stream_accum<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt, acc);
-  }
+  const int lane = t & 63, w = wave_id();
+  if (t == 0) sm.p.s_gate = 0ull;  // ordered before its uses by the barriers below
+  int cnt0 = 0;
+  if (g0 != 0xffffffffu) cnt0 = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, g0 - 1u, -1, sm.p.list, sm.p.wcnt);
+  constexpr int STEP = sl::proddev::step_columns<LPC, 8, FT>();
+  const int nsteps = (cnt0 + STEP - 1) / STEP;  // workgroup-uniform
 
-  if (t == 0) {
-    uint64_t v = 0ull;
-    for (uint32_t it = 0; it < kSpinLimit; ++it) {
-      v = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (v != 0ull) break;
-      __builtin_amdgcn_s_sleep(1);
+  // The speculative list, over all wavefronts' column slots. Each wavefront
+  // issues its poll of the flag just before its last step's loads: loads
+  // complete in order, so the answer is in when that step's weights are.
+  uint64_t pv = 0ull;
+  for (int it = 0; it < nsteps; ++it) {
+    if (it == nsteps - 1 && lane == 0) pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    sl::proddev::stream_step<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, it, acc);
+  }
+  if (nsteps == 0) {
+    // nothing to stream ahead of the gate: one thread waits for the pair
+    if (t == 0) {
+      for (uint32_t it = 0; it < kSpinLimit; ++it) {
+        pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (pv != 0ull) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      sm.p.s_gate = pv;
     }
-    if (v == 0ull) __hip_atomic_store(&sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm.p.s_gate = v;
+    __syncthreads();
+    pv = sm.p.s_gate;
+  } else {
+    // a wavefront whose early poll came back empty waits: wavefront 0 polls
+    // memory (one poller per workgroup: a poll storm on one line would stall
+    // the weight stream), the others watch its copy in LDS; kGateTimeout
+    // marks a wait that gave up
+    if (lane == 0) {
+      if (pv != 0ull) {
+        __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else if (w == 0) {
+        for (uint32_t it = 0; pv == 0ull && it < kSpinLimit; ++it) {
+          __builtin_amdgcn_s_sleep(2);
+          pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (pv == 0ull) pv = kGateTimeout;
+        __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        for (uint32_t it = 0; pv == 0ull && it < 4u * kSpinLimit; ++it) {
+          __builtin_amdgcn_s_sleep(1);
+          pv = __hip_atomic_load(&sm.p.s_gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      }
+    }
+    pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pv >> 32), 0) << 32) |
+         (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pv, 0);
+    if (pv == kGateTimeout) pv = 0ull;
   }
-  __syncthreads();
-  const uint64_t v = sm.p.s_gate;
-  if (v == 0ull) {  // timed out: recorded in the error word
-    if (t == 0)
-      __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return;
-  }
-  const uint32_t kthr = (uint32_t)v;
-  const int jlast = (int)(uint32_t)(v >> 32) - 2;
-  // every speculated input is kept iff the bound lies above the threshold
-  // key; otherwise the speculative sums are dropped and everything is redone
-  uint32_t below = g0;
-  if (g0 != 0xffffffffu && g0 <= kthr) {
-#pragma unroll
-    for (int q = 0; q < sl::proddev::Acc<WT>::VEC; ++q) acc.v[q] = 0.f;
-    below = 0xffffffffu;
-  }
-  const int cnt = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, kthr, jlast, sm.p.list, sm.p.wcnt, below);
-  // acknowledged after the chunk's loads have been consumed, so that waiting
-  // for the atomic overlaps the weight loads instead of delaying them
-  if (t == 0)
+  if (t == 0) {
+    if (pv == 0ull) __hip_atomic_store(&sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  sl::proddev::stream_accum<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt, acc);
+  }
+  if (pv != 0ull) {  // (0: the wait timed out, recorded in the error word)
+    const uint32_t kthr = (uint32_t)pv;
+    const int jlast = (int)(uint32_t)(pv >> 32) - 2;
+    // every speculated input is kept iff the bound lies above the threshold
+    // key; otherwise the speculative sums are dropped and all kept inputs
+    // are streamed
+    const bool valid = g0 == 0xffffffffu || g0 > kthr;
+    if (!valid) {
+#pragma unroll
+      for (int q = 0; q < sl::proddev::Acc<WT>::VEC; ++q) acc.v[q] = 0.f;
+    }
+    // the rest: each wavefront streams the kept inputs among its own 64 (one
+    // per lane) that the speculation did not cover, into its own slots
+    const int j = j0 + t;
+    const bool rest = j < j1 && gate_keep(ch.kv[0], j, kthr, jlast) && (!valid || ch.kv[0] < g0);
+    sl::proddev::stream_wave_bits<WT, LPC, 8>(Wt, m, tile, j0 + 64 * w, __ballot(rest), ch.xv[0], acc);
+  }
   sl::proddev::reduce_out<WT, YT, LPC, FT, ATOMIC>(acc, m, tile, split, splits, sm.p.red, partials, ctr,
                                                    &sm.p.s_last, y);
 }

@@ -106,22 +106,31 @@ struct Acc {
   float v[VEC];
 };
 
-// Streams the row-tile runs of list[0 .. cnt) into acc (added to what it
-// holds).
-template <typename WT, int LPC, int U, int PT>
-__device__ __forceinline__ void stream_accum(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
-                                             Acc<WT>& a) {
+// Columns one stream step covers: each of the CS column slots of the
+// workgroup takes up to U list entries.
+template <int LPC, int U, int PT>
+constexpr int step_columns() {
+  return (PT / 64) * (64 / LPC) * U;
+}
+
+// One stream step: list entries it * step_columns() .. + step_columns()
+// (those below cnt) into acc. Each slot issues its U loads before consuming
+// any.
+template <typename WT, int LPC, int U, int PT, int NWS = PT / 64>
+__device__ __forceinline__ void stream_step(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
+                                            int it, Acc<WT>& a) {
   constexpr int VEC = Acc<WT>::VEC;          // elements per 16-byte run
   constexpr int R = LPC * VEC;               // rows per tile
   constexpr int CPW = 64 / LPC;              // column slots per wavefront
-  constexpr int CS = (PT / 64) * CPW;        // column slots per workgroup
+  constexpr int CS = NWS * CPW;              // column slots of the NWS streaming wavefronts
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const int slot = w * CPW + lane / LPC;
   const int sub = lane % LPC;
   const int row = tile * R + sub * VEC;
-  if (row >= m) return;
+  const int k0 = slot + it * CS * U;
+  if (row >= m || k0 >= cnt) return;
   const WT* base = Wt + row;
-  for (int k0 = slot; k0 < cnt; k0 += CS * U) {
+  {
     int2 e[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -138,6 +147,63 @@ __device__ __forceinline__ void stream_accum(const WT* __restrict__ Wt, int m, i
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) fma_run(a.v, wv[u], k0 + u * CS < cnt ? __int_as_float(e[u].y) : 0.f);
+  }
+}
+
+// Streams the row-tile runs of list[0 .. cnt) into acc (added to what it
+// holds), over the column slots of wavefronts 0 .. NWS-1 (the calling
+// wavefront must be one of them).
+template <typename WT, int LPC, int U, int PT, int NWS = PT / 64>
+__device__ __forceinline__ void stream_accum(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
+                                             Acc<WT>& a) {
+  constexpr int STEP = NWS * (64 / LPC) * U;
+  for (int it = 0; it * STEP < cnt; ++it) stream_step<WT, LPC, U, PT, NWS>(Wt, m, tile, list, cnt, it, a);
+}
+
+// Streams into acc the columns jbase + b for every set bit b of the
+// wavefront-uniform mask bal (the inputs of this wavefront's 64 lanes); the
+// x of input jbase + b is lane b's xv. The CPW column slots of the
+// wavefront take the set bits in turn, U per slot in flight together.
+template <typename WT, int LPC, int U>
+__device__ __forceinline__ void stream_wave_bits(const WT* __restrict__ Wt, int m, int tile, int jbase, uint64_t bal,
+                                                 float xv, Acc<WT>& a) {
+  constexpr int VEC = Acc<WT>::VEC;
+  constexpr int R = LPC * VEC;
+  constexpr int CPW = 64 / LPC;
+  constexpr int B = CPW * U;  // set bits per batch
+  const int lane = threadIdx.x & 63, sw = lane / LPC;
+  const int row = tile * R + (lane % LPC) * VEC;
+  const bool rok = row < m;
+  const WT* base = Wt + (rok ? row : 0);
+  while (bal != 0ull) {
+    int bi[B];
+    float xs[B];
+#pragma unroll
+    for (int i = 0; i < B; ++i) {  // scalar: the next set bit and its x
+      const int b = bal != 0ull ? (int)__builtin_ctzll(bal) : -1;
+      bal = bal != 0ull ? bal & (bal - 1ull) : 0ull;
+      bi[i] = b;
+      xs[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), b < 0 ? 0 : b));
+    }
+    u32x4 wv[U];
+    float xu[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int b = -1;
+      float xx = 0.f;
+#pragma unroll
+      for (int q = 0; q < CPW; ++q)
+        if (sw == q) {
+          b = bi[u * CPW + q];
+          xx = xs[u * CPW + q];
+        }
+      const bool ok = b >= 0 && rok;
+      wv[u] = ok ? __builtin_nontemporal_load((const u32x4*)(base + (size_t)(jbase + b) * (size_t)m))
+                 : u32x4{0u, 0u, 0u, 0u};
+      xu[u] = ok ? xx : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) fma_run(a.v, wv[u], xu[u]);
   }
 }
 
