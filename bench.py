@@ -51,6 +51,9 @@ def parse():
                     help="restrict the measured legs (short profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for memory counters)")
+    ap.add_argument("--counters-run", action="store_true",
+                    help="short eager run for memory-counter passes: 12 + 48 headline forwards "
+                         "(K=5504), then three plain 256 MiB device copies; prints one line")
     ap.add_argument("--workload", default="llama7b_down",
                     choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16"],
                     help="llama7b_down is the headline; the others measure the remaining layer shapes")
@@ -100,6 +103,9 @@ def main():
 
     if args.workload != "llama7b_down":
         run_workload(args)
+        return
+    if args.counters_run:
+        counters_run()
         return
 
     import numpy as np
@@ -250,9 +256,18 @@ def main():
         ring = make_ring(Ks["sparse50"])
         secs = run_steps(layer_step(ring, True), args.steps, args.warmup)
         _, prod_us, _, _ = kernel_times(ring, True)
+        # the ordered split reduction needs no clearing of y (no fill kernel
+        # before the product): the speedup is taken against the faster form
+        for h in ring:
+            h.set_deterministic(True)
+        ordered_us = time_graph(layer_step(ring, True))
+        for h in ring:
+            h.set_deterministic(False)
         ab = algorithmic_bytes(m, n, n)
+        best_us = min(secs / args.steps * 1e6, ordered_us)
         dense = {"tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
-                 "product_kernel_us": prod_us, "achieved_GBps": ab / (prod_us * 1e-6) / 1e9}
+                 "product_kernel_us": prod_us, "achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
+                 "ordered_reduction_us_per_step": ordered_us, "best_us_per_step": best_us}
         for h in ring:
             h.close()
         del ring
@@ -330,7 +345,7 @@ def main():
         out["dense_same_kernel"] = {k: round(v, 4) for k, v in dense.items()}
         for k, v in results.items():
             bar = 0.8 / (1 - v["sparsity"])
-            out["legs"][k]["speedup_vs_dense"] = round(v["tokens_per_s"] / dense["tokens_per_s"], 4)
+            out["legs"][k]["speedup_vs_dense"] = round(v["tokens_per_s"] * dense["best_us_per_step"] * 1e-6, 4)
             out["legs"][k]["speedup_bar"] = round(bar, 4)
     out["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(out))
@@ -507,6 +522,39 @@ def _graph_us(torch, fn, count=240):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / count
+
+
+def counters_run():
+    """Few dispatches, for rocprofv3 --pmc passes (each dispatch is profiled
+    on its own): 60 eager headline forwards over the 12-copy ring, then a plain
+    256 MiB device-to-device copy three times, whose counters calibrate the
+    byte scale."""
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    m, n, K = 4096, 11008, wl.k_from_sparsity(11008, 0.5)
+    Wd = torch.from_numpy(wl.weight(2, 0).view(np.int16)).to(dev).view(torch.bfloat16)
+    X = torch.from_numpy(wl.tokens(2, 0, 0, NTOK).view(np.int16)).to(dev).view(torch.bfloat16).contiguous()
+    ring = [fas.SparseLinear(Wd, c=None, gate="topk", K=K) for _ in range(RING)]
+    Y = torch.empty((RING, m), dtype=torch.float32, device=dev)
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(60):
+        fas.sparse_linear_forward(ring[i % RING].handle, X[i % NTOK].data_ptr(), 1, Y[i % RING].data_ptr(),
+                                  fas.SL_F32, 0, 0, 0, s)
+    torch.cuda.synchronize()
+    a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    for h in ring:
+        h.sync_status()
+    print(json.dumps({"counters_run": "done", "forwards": 60, "K": K, "copy_bytes": 256 << 20}))
 
 
 def cpu_baseline(wl, Wh, K, seconds):
