@@ -143,71 +143,94 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
 
   // The speculative list, over all wavefronts' column slots. Each wavefront
   // issues its poll of the flag just before its last step's loads: loads
-  // complete in order, so the answer is in when that step's weights are.
+  // complete in order, so the answer is in before that step's weights are.
+  // When the pair is there and the speculation holds, the first batch of the
+  // rest (the kept inputs among the wavefront's own 64 that the speculation
+  // did not cover) is issued before the last step's weights are consumed.
   uint64_t pv = 0ull;
-  for (int it = 0; it < nsteps; ++it) {
-    if (it == nsteps - 1 && lane == 0) pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  bool rest_done = false;  // wavefront-uniform
+  const int jw = j0 + 64 * w;
+  const int jt = j0 + t;
+  for (int it = 0; it + 1 < nsteps; ++it) sl::proddev::stream_step<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, it, acc);
+  if (nsteps > 0) {
+    if (lane == 0) pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    sl::proddev::stream_step<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, it, acc);
-  }
-  if (nsteps == 0) {
-    // nothing to stream ahead of the gate: one thread waits for the pair
-    if (t == 0) {
-      for (uint32_t it = 0; it < kSpinLimit; ++it) {
-        pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (pv != 0ull) break;
-        __builtin_amdgcn_s_sleep(1);
-      }
-      sm.p.s_gate = pv;
-    }
-    __syncthreads();
-    pv = sm.p.s_gate;
-  } else {
-    // a wavefront whose early poll came back empty waits: wavefront 0 polls
-    // memory (one poller per workgroup: a poll storm on one line would stall
-    // the weight stream), the others watch its copy in LDS; kGateTimeout
-    // marks a wait that gave up
-    if (lane == 0) {
-      if (pv != 0ull) {
-        __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else if (w == 0) {
-        for (uint32_t it = 0; pv == 0ull && it < kSpinLimit; ++it) {
-          __builtin_amdgcn_s_sleep(2);
-          pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (pv == 0ull) pv = kGateTimeout;
-        __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      } else {
-        for (uint32_t it = 0; pv == 0ull && it < 4u * kSpinLimit; ++it) {
-          __builtin_amdgcn_s_sleep(1);
-          pv = __hip_atomic_load(&sm.p.s_gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        }
-      }
-    }
+    sl::proddev::Batch<WT, 8> last, rest;
+    sl::proddev::step_issue<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, nsteps - 1, last);
     pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pv >> 32), 0) << 32) |
          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pv, 0);
-    if (pv == kGateTimeout) pv = 0ull;
+    uint64_t bal = 0ull;
+    bool any = false;
+    if (pv != 0ull && g0 > (uint32_t)pv) {  // pair known and the speculation holds
+      const uint32_t kthr = (uint32_t)pv;
+      const int jlast = (int)(uint32_t)(pv >> 32) - 2;
+      bal = __ballot(jt < j1 && gate_keep(ch.kv[0], jt, kthr, jlast) && ch.kv[0] < g0);
+      any = bal != 0ull;
+      if (any) sl::proddev::bits_issue<WT, LPC, 8>(Wt, m, tile, jw, bal, ch.xv[0], rest);
+      rest_done = true;
+    }
+    if (lane == 0 && pv != 0ull) __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    sl::proddev::step_consume<WT, 8>(last, acc);
+    if (any) sl::proddev::step_consume<WT, 8>(rest, acc);
+    if (rest_done) sl::proddev::stream_wave_bits<WT, LPC, 8>(Wt, m, tile, jw, bal, ch.xv[0], acc);  // leftovers
+  }
+  if (!rest_done) {
+    if (nsteps == 0) {
+      // nothing to stream ahead of the gate: one thread waits for the pair
+      if (t == 0) {
+        for (uint32_t it = 0; it < kSpinLimit; ++it) {
+          pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (pv != 0ull) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        sm.p.s_gate = pv;
+      }
+      __syncthreads();
+      pv = sm.p.s_gate;
+    } else if (pv == 0ull) {
+      // the early poll came back empty: wavefront 0 polls memory (one poller
+      // per workgroup: a poll storm on one line would stall the weight
+      // stream), the others watch its copy in LDS; kGateTimeout marks a wait
+      // that gave up
+      if (lane == 0) {
+        if (w == 0) {
+          for (uint32_t it = 0; pv == 0ull && it < kSpinLimit; ++it) {
+            __builtin_amdgcn_s_sleep(2);
+            pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          if (pv == 0ull) pv = kGateTimeout;
+          __hip_atomic_store(&sm.p.s_gate, pv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        } else {
+          for (uint32_t it = 0; pv == 0ull && it < 4u * kSpinLimit; ++it) {
+            __builtin_amdgcn_s_sleep(1);
+            pv = __hip_atomic_load(&sm.p.s_gate, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          }
+        }
+      }
+      pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pv >> 32), 0) << 32) |
+           (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pv, 0);
+      if (pv == kGateTimeout) pv = 0ull;
+    }
+    if (pv != 0ull) {  // (0: the wait timed out, recorded in the error word)
+      const uint32_t kthr = (uint32_t)pv;
+      const int jlast = (int)(uint32_t)(pv >> 32) - 2;
+      // every speculated input is kept iff the bound lies above the
+      // threshold key; otherwise the speculative sums are dropped and all
+      // kept inputs are streamed
+      const bool valid = g0 == 0xffffffffu || g0 > kthr;
+      if (!valid) {
+#pragma unroll
+        for (int q = 0; q < sl::proddev::Acc<WT>::VEC; ++q) acc.v[q] = 0.f;
+      }
+      // the rest: each wavefront streams the kept inputs among its own 64
+      // (one per lane) that the speculation did not cover, into its own slots
+      const bool rest = jt < j1 && gate_keep(ch.kv[0], jt, kthr, jlast) && (!valid || ch.kv[0] < g0);
+      sl::proddev::stream_wave_bits<WT, LPC, 8>(Wt, m, tile, jw, __ballot(rest), ch.xv[0], acc);
+    }
   }
   if (t == 0) {
     if (pv == 0ull) __hip_atomic_store(&sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if (pv != 0ull) {  // (0: the wait timed out, recorded in the error word)
-    const uint32_t kthr = (uint32_t)pv;
-    const int jlast = (int)(uint32_t)(pv >> 32) - 2;
-    // every speculated input is kept iff the bound lies above the threshold
-    // key; otherwise the speculative sums are dropped and all kept inputs
-    // are streamed
-    const bool valid = g0 == 0xffffffffu || g0 > kthr;
-    if (!valid) {
-#pragma unroll
-      for (int q = 0; q < sl::proddev::Acc<WT>::VEC; ++q) acc.v[q] = 0.f;
-    }
-    // the rest: each wavefront streams the kept inputs among its own 64 (one
-    // per lane) that the speculation did not cover, into its own slots
-    const int j = j0 + t;
-    const bool rest = j < j1 && gate_keep(ch.kv[0], j, kthr, jlast) && (!valid || ch.kv[0] < g0);
-    sl::proddev::stream_wave_bits<WT, LPC, 8>(Wt, m, tile, j0 + 64 * w, __ballot(rest), ch.xv[0], acc);
   }
   sl::proddev::reduce_out<WT, YT, LPC, FT, ATOMIC>(acc, m, tile, split, splits, sm.p.red, partials, ctr,
                                                    &sm.p.s_last, y);

@@ -113,41 +113,60 @@ constexpr int step_columns() {
   return (PT / 64) * (64 / LPC) * U;
 }
 
-// One stream step: list entries it * step_columns() .. + step_columns()
-// (those below cnt) into acc. Each slot issues its U loads before consuming
-// any.
+// Weights and inputs of one in-flight batch: U 16-byte runs per lane and
+// the x each multiplies (0 where the slot has no column).
+template <typename WT, int U>
+struct Batch {
+  u32x4 wv[U];
+  float xs[U];
+};
+
+// Issues one stream step: list entries it * CS * U .. + CS * U (those below
+// cnt), slot s taking entries s, s + CS, ... of the step (CS = NWS * CPW
+// column slots of the NWS streaming wavefronts).
 template <typename WT, int LPC, int U, int PT, int NWS = PT / 64>
-__device__ __forceinline__ void stream_step(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
-                                            int it, Acc<WT>& a) {
+__device__ __forceinline__ void step_issue(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
+                                           int it, Batch<WT, U>& b) {
   constexpr int VEC = Acc<WT>::VEC;          // elements per 16-byte run
   constexpr int R = LPC * VEC;               // rows per tile
   constexpr int CPW = 64 / LPC;              // column slots per wavefront
   constexpr int CS = NWS * CPW;              // column slots of the NWS streaming wavefronts
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const int slot = w * CPW + lane / LPC;
-  const int sub = lane % LPC;
-  const int row = tile * R + sub * VEC;
+  const int row = tile * R + (lane % LPC) * VEC;
   const int k0 = slot + it * CS * U;
-  if (row >= m || k0 >= cnt) return;
-  const WT* base = Wt + row;
-  {
-    int2 e[U];
+  const bool rok = row < m;
+  const WT* base = Wt + (rok ? row : 0);
+  int2 e[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k = k0 + u * CS;
-      e[u] = list[k < cnt ? k : k0];
-    }
-    u32x4 wv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (k0 + u * CS < cnt)
-        wv[u] = __builtin_nontemporal_load((const u32x4*)(base + (size_t)e[u].x * (size_t)m));
-      else
-        wv[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) fma_run(a.v, wv[u], k0 + u * CS < cnt ? __int_as_float(e[u].y) : 0.f);
+  for (int u = 0; u < U; ++u) {
+    const int k = k0 + u * CS;
+    e[u] = list[k < cnt ? k : 0];
   }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = rok && k0 + u * CS < cnt;
+    b.wv[u] = ok ? __builtin_nontemporal_load((const u32x4*)(base + (size_t)e[u].x * (size_t)m))
+                 : u32x4{0u, 0u, 0u, 0u};
+    b.xs[u] = ok ? __int_as_float(e[u].y) : 0.f;
+  }
+}
+
+template <typename WT, int U>
+__device__ __forceinline__ void step_consume(const Batch<WT, U>& b, Acc<WT>& a) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) fma_run(a.v, b.wv[u], b.xs[u]);
+}
+
+// One stream step: list entries it * step_columns() .. + step_columns()
+// (those below cnt) into acc. Each slot issues its U loads before consuming
+// any.
+template <typename WT, int LPC, int U, int PT, int NWS = PT / 64>
+__device__ __forceinline__ void stream_step(const WT* __restrict__ Wt, int m, int tile, const int2* list, int cnt,
+                                            int it, Acc<WT>& a) {
+  Batch<WT, U> b;
+  step_issue<WT, LPC, U, PT, NWS>(Wt, m, tile, list, cnt, it, b);
+  step_consume<WT, U>(b, a);
 }
 
 // Streams the row-tile runs of list[0 .. cnt) into acc (added to what it
@@ -160,13 +179,13 @@ __device__ __forceinline__ void stream_accum(const WT* __restrict__ Wt, int m, i
   for (int it = 0; it * STEP < cnt; ++it) stream_step<WT, LPC, U, PT, NWS>(Wt, m, tile, list, cnt, it, a);
 }
 
-// Streams into acc the columns jbase + b for every set bit b of the
-// wavefront-uniform mask bal (the inputs of this wavefront's 64 lanes); the
-// x of input jbase + b is lane b's xv. The CPW column slots of the
-// wavefront take the set bits in turn, U per slot in flight together.
+// Issues one batch of the columns jbase + b for the set bits b of the
+// wavefront-uniform mask bal (the inputs of this wavefront's 64 lanes),
+// removing them from bal; the x of input jbase + b is lane b's xv. The CPW
+// column slots of the wavefront take the set bits in turn, U per slot.
 template <typename WT, int LPC, int U>
-__device__ __forceinline__ void stream_wave_bits(const WT* __restrict__ Wt, int m, int tile, int jbase, uint64_t bal,
-                                                 float xv, Acc<WT>& a) {
+__device__ __forceinline__ void bits_issue(const WT* __restrict__ Wt, int m, int tile, int jbase, uint64_t& bal,
+                                           float xv, Batch<WT, U>& bt) {
   constexpr int VEC = Acc<WT>::VEC;
   constexpr int R = LPC * VEC;
   constexpr int CPW = 64 / LPC;
@@ -175,35 +194,40 @@ __device__ __forceinline__ void stream_wave_bits(const WT* __restrict__ Wt, int 
   const int row = tile * R + (lane % LPC) * VEC;
   const bool rok = row < m;
   const WT* base = Wt + (rok ? row : 0);
+  int bi[B];
+  float xs[B];
+#pragma unroll
+  for (int i = 0; i < B; ++i) {  // scalar: the next set bit and its x
+    const int b = bal != 0ull ? (int)__builtin_ctzll(bal) : -1;
+    bal = bal != 0ull ? bal & (bal - 1ull) : 0ull;
+    bi[i] = b;
+    xs[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), b < 0 ? 0 : b));
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    int b = -1;
+    float xx = 0.f;
+#pragma unroll
+    for (int q = 0; q < CPW; ++q)
+      if (sw == q) {
+        b = bi[u * CPW + q];
+        xx = xs[u * CPW + q];
+      }
+    const bool ok = b >= 0 && rok;
+    bt.wv[u] = ok ? __builtin_nontemporal_load((const u32x4*)(base + (size_t)(jbase + b) * (size_t)m))
+                  : u32x4{0u, 0u, 0u, 0u};
+    bt.xs[u] = ok ? xx : 0.f;
+  }
+}
+
+// Streams into acc the columns of every set bit of bal (see bits_issue).
+template <typename WT, int LPC, int U>
+__device__ __forceinline__ void stream_wave_bits(const WT* __restrict__ Wt, int m, int tile, int jbase, uint64_t bal,
+                                                 float xv, Acc<WT>& a) {
   while (bal != 0ull) {
-    int bi[B];
-    float xs[B];
-#pragma unroll
-    for (int i = 0; i < B; ++i) {  // scalar: the next set bit and its x
-      const int b = bal != 0ull ? (int)__builtin_ctzll(bal) : -1;
-      bal = bal != 0ull ? bal & (bal - 1ull) : 0ull;
-      bi[i] = b;
-      xs[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(xv), b < 0 ? 0 : b));
-    }
-    u32x4 wv[U];
-    float xu[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      int b = -1;
-      float xx = 0.f;
-#pragma unroll
-      for (int q = 0; q < CPW; ++q)
-        if (sw == q) {
-          b = bi[u * CPW + q];
-          xx = xs[u * CPW + q];
-        }
-      const bool ok = b >= 0 && rok;
-      wv[u] = ok ? __builtin_nontemporal_load((const u32x4*)(base + (size_t)(jbase + b) * (size_t)m))
-                 : u32x4{0u, 0u, 0u, 0u};
-      xu[u] = ok ? xx : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) fma_run(a.v, wv[u], xu[u]);
+    Batch<WT, U> bt;
+    bits_issue<WT, LPC, U>(Wt, m, tile, jbase, bal, xv, bt);
+    step_consume<WT, U>(bt, a);
   }
 }
 
