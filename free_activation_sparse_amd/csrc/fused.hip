@@ -32,6 +32,7 @@ using namespace sl::dev;
 constexpr int FT = sl::gatedev::GT;  // threads per workgroup (16 wavefronts)
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls (>= 50 ns each) before giving up
 constexpr float kSpecMargin = 1.15f;       // speculation bound over the previous threshold score
+constexpr uint32_t kPartsWait = 2000;      // s_memrealtime ticks (20 us) the gate waits for moment parts
 
 struct GateSmem {
   alignas(16) uint32_t h1[4096];
@@ -40,7 +41,7 @@ struct GateSmem {
   uint64_t cand[64];
   uint32_t wsum[FT / 64];
   uint32_t res[4];
-  sl::gatedev::dd dsum[FT / 64][2];
+  sl::gatedev::sd dsum[FT / 64][2];
   uint32_t kminmax[FT / 64][2];
 };
 
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
                                                    int32_t* __restrict__ count_out, double* __restrict__ thresh_out,
                                                    int tiles, int splits, int chunk, float* __restrict__ partials,
                                                    uint32_t* __restrict__ ctr, sl::FusedSync* __restrict__ sync,
-                                                   YT* __restrict__ y) {
+                                                   int use_parts, YT* __restrict__ y) {
   __shared__ union {
     GateSmem g;
     ProdSmem<WT> p;
@@ -84,9 +85,12 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
     uint32_t kthr;
     int jlast;
     float* zy = (ATOMIC && splits > 1) ? (float*)y : nullptr;
+    const uint32_t gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sl::gatedev::PartsIn pin{};
+    if (MODE == sl::gatedev::MODE_STAT && use_parts) pin = {sync->parts, (n + 63) / 64, gen + 1u, kPartsWait};
     sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, 0.0f, gout, mask_out, count_out, thresh_out, zy, m,
                                               sm.g.h1, sm.g.h2, sm.g.h3, sm.g.wsum, sm.g.res, sm.g.cand,
-                                              sm.g.dsum, sm.g.kminmax, 0, kthr, jlast);
+                                              sm.g.dsum, sm.g.kminmax, 0, pin, kthr, jlast);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
     __syncthreads();
     if (t == 0) __hip_atomic_store(&sync->flag, pack_gate(kthr, jlast), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -107,6 +111,9 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
         __hip_atomic_store(&sync->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t < sl::kAckSlots) __hip_atomic_store(&sync->ack[16 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t == 0) __hip_atomic_store(&sync->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // a new tag for the next launch's moment parts: anything written
+      // under this one (late or not) no longer counts
+      if (t == 0) __hip_atomic_store(&sync->gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -119,9 +126,38 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   // the handle's previous threshold key (any value read here is safe: it only
   // steers the speculation below, which is checked against the exact pair)
   const uint32_t prevk = SPEC ? __hip_atomic_load(&gout->kthr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  // the tag for this launch's moment parts (statistical gate)
+  const uint32_t gen = MODE == sl::gatedev::MODE_STAT && use_parts
+                           ? __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0u;
   static_assert(sl::proddev::Chunk<FT>::ROUNDS == 1, "one input per thread");
   sl::proddev::Chunk<FT> ch;
   sl::proddev::load_chunk<WT, FT, false>(x, c, j0, j1, ch);
+  const int lane = t & 63, w = wave_id();
+  const int jt = j0 + t;
+  if (MODE == sl::gatedev::MODE_STAT && use_parts) {
+    // Statistical gate: the moment sums of the token's scores come from
+    // here, one part per 64-input slice of the chunk (chunks start at
+    // multiples of 64), each summed by one wavefront of one row tile's
+    // workgroup and stored before the weight stream loads the memory
+    // system; the gate workgroup adds the parts in index order.
+    const int nsl = (j1 - j0 + 63) >> 6;
+    if (w < nsl && w % tiles == tile) {
+      const bool valid = jt < j1;
+      const double s = valid ? (double)__uint_as_float(ch.kv[0]) : 0.0;
+      sl::gatedev::sd S1{s, 0.0}, S2{s * s, 0.0};  // squares of fp32 values are exact in fp64
+      sl::gatedev::wave_sum_sd(S1, S2);
+      const uint32_t kmax = wave_max(valid ? ch.kv[0] : 0u);
+      const uint32_t kmin = ~wave_max(valid ? ~ch.kv[0] : 0u);
+      if (lane < sl::kMomentWords) {
+        // lane k stores word k: payload in the low half, the tag above it
+        const uint64_t d = (uint64_t)__double_as_longlong(lane < 2 ? S1.hi : lane < 4 ? S1.lo : lane < 6 ? S2.hi : S2.lo);
+        const uint32_t pl = lane == 8 ? kmin : lane == 9 ? kmax : (uint32_t)(d >> (32 * (lane & 1)));
+        __hip_atomic_store(&sync->parts[(j0 >> 6) + w].w[lane], ((uint64_t)(gen + 1u) << 32) | pl,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
   sl::proddev::Acc<WT> acc;
 #pragma unroll
   for (int v = 0; v < sl::proddev::Acc<WT>::VEC; ++v) acc.v[v] = 0.f;
@@ -134,7 +170,6 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
     g0 = __float_as_uint(__uint_as_float(prevk) * kSpecMargin);
     if (g0 <= prevk) g0 = prevk + 1u;
   }
-  const int lane = t & 63, w = wave_id();
   if (t == 0) sm.p.s_gate = 0ull;  // ordered before its uses by the barriers below
   int cnt0 = 0;
   if (g0 != 0xffffffffu) cnt0 = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, g0 - 1u, -1, sm.p.list, sm.p.wcnt);
@@ -150,7 +185,6 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   uint64_t pv = 0ull;
   bool rest_done = false;  // wavefront-uniform
   const int jw = j0 + 64 * w;
-  const int jt = j0 + t;
   for (int it = 0; it + 1 < nsteps; ++it) sl::proddev::stream_step<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, it, acc);
   if (nsteps > 0) {
     if (lane == 0) pv = __hip_atomic_load(&sync->flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -243,7 +277,7 @@ struct FusedPlan {
 // Row tiles of LPC * 8 rows; the input chunks are sized so that the product
 // workgroups fill the device's remaining workgroup slots once (chunks of
 // 32..kMaxChunk inputs), unless a split count is forced on the handle.
-FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu) {
+FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu, int align) {
   FusedPlan p;
   const int64_t n = h->n;
   const int rows = lpc * 8;
@@ -253,6 +287,7 @@ FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu) {
   splits = std::min<int64_t>(splits, std::min<int64_t>(sl::kMaxSplits, (n + 31) / 32));
   splits = std::max<int64_t>(splits, (n + sl::kMaxChunk - 1) / sl::kMaxChunk);
   p.chunk = (int)((n + splits - 1) / splits);
+  p.chunk = (p.chunk + align - 1) / align * align;  // kMaxChunk is a multiple of align
   p.splits = (int)((n + p.chunk - 1) / p.chunk);
   return p;
 }
@@ -267,10 +302,14 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
       nb = 1;
     return std::max(1, nb);
   }();
-  const FusedPlan p = plan_fused(h, LPC, per_cu);
+  // the statistical gate's moment parts cover 64-input slices that must not straddle chunks
+  const FusedPlan p = plan_fused(h, LPC, per_cu, MODE == sl::gatedev::MODE_STAT ? 64 : 1);
+  // moment parts only when every workgroup of the launch can be resident at
+  // once (the gate would otherwise wait for workgroups not yet dispatched)
+  const int use_parts = 1 + (int64_t)p.tiles * p.splits <= (int64_t)std::max(1, h->cus) * per_cu ? 1 : 0;
   fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(
       (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, (int)h->m, (int)h->n, (int)h->K, h->z, g, mask, cnt,
-      th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, (YT*)y);
+      th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, use_parts, (YT*)y);
   return hipGetLastError();
 }
 
@@ -278,6 +317,11 @@ template <typename YT, int G, int MODE, bool ATOMIC>
 hipError_t go_lpc(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt,
                   double* th, void* y, hipStream_t s) {
   int lpc = h->plan_rows > 0 ? h->plan_rows / 8 : (h->m >= 8192 ? 64 : (h->m >= 2048 ? 32 : 16));
+  // taller row tiles when the chunk limit alone would ask for more product
+  // workgroups than the device holds at once (a late tail of workgroups)
+  const int64_t min_splits = (h->n + sl::kMaxChunk - 1) / sl::kMaxChunk;
+  while (h->plan_rows <= 0 && lpc < 64 && (h->m + 8 * lpc - 1) / (8 * lpc) * min_splits >= std::max(1, h->cus))
+    lpc *= 2;
   switch (lpc) {
     case 16: return go<YT, G, MODE, 16, ATOMIC>(h, x, g, mask, cnt, th, y, s);
     case 32: return go<YT, G, MODE, 32, ATOMIC>(h, x, g, mask, cnt, th, y, s);

@@ -21,16 +21,16 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
   __shared__ uint64_t cand[MODE == MODE_TOPK ? 64 : 1];
   __shared__ uint32_t wsum[GW];
   __shared__ uint32_t res[4];
-  __shared__ dd dsum[MODE == MODE_STAT ? GW : 1][2];
+  __shared__ sd dsum[MODE == MODE_STAT ? GW : 1][2];
   __shared__ uint32_t kminmax[MODE == MODE_STAT ? GW : 1][2];
   uint32_t kthr;
   int jlast;
   if (vec)
     gate_body<XT, G, MODE, true>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2, h3,
-                                 wsum, res, cand, dsum, kminmax, blockIdx.x, kthr, jlast);
+                                 wsum, res, cand, dsum, kminmax, blockIdx.x, PartsIn{}, kthr, jlast);
   else
     gate_body<XT, G, MODE, false>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2,
-                                  h3, wsum, res, cand, dsum, kminmax, blockIdx.x, kthr, jlast);
+                                  h3, wsum, res, cand, dsum, kminmax, blockIdx.x, PartsIn{}, kthr, jlast);
 }
 
 template <typename XT, int G>

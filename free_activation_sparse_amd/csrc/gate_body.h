@@ -12,8 +12,10 @@
 //    bin, i.e. heavy ties): radix select on 12/12/7-bit key digits, then the
 //    kept ties' last index by a radix select on the index (8/7 bits).
 //  * Statistical threshold (Spark Transformer article, section 2.2): mean and
-//    population variance of the scores in double-double arithmetic, each
-//    rounded once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)).
+//    population variance of the scores from double-double sums, each rounded
+//    once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)). The sums
+//    come from this workgroup's own scores, or (fused forward) from partial
+//    sums of 64-input slices that the product workgroups publish.
 //  * Fixed threshold: kthr from the per-layer tau (WINA article, section 三,
 //    calibrated per-layer thresholds).
 //
@@ -160,12 +162,17 @@ __device__ __forceinline__ dd dd_add(dd a, dd b) {
   dd u = fast_two_sum(s.hi, s.lo + t.hi);
   return fast_two_sum(u.hi, u.lo + t.lo);
 }
-__device__ __forceinline__ dd dd_div(dd a, double b) {
-  const double q1 = a.hi / b;
-  double r = fma(-q1, b, a.hi);  // exact remainder
-  r = r + a.lo;
-  const double q2 = r / b;
-  return fast_two_sum(q1, q2);
+// 1/b as a double-double (the fma remainder is exact): ~2^-106 relative.
+__device__ __forceinline__ dd dd_recip(double b) {
+  const double h = 1.0 / b;
+  return {h, fma(-h, b, 1.0) / b};
+}
+// a * r for a double-double reciprocal r: ~2^-104 relative, no division.
+__device__ __forceinline__ dd dd_mul(dd a, dd r) {
+  const double p = a.hi * r.hi;
+  double e = fma(a.hi, r.hi, -p);  // exact error of the product
+  e = e + (a.hi * r.lo + a.lo * r.hi);
+  return fast_two_sum(p, e);
 }
 __device__ __forceinline__ dd dd_sqr(dd a) {
   const double p = a.hi * a.hi;
@@ -173,9 +180,104 @@ __device__ __forceinline__ dd dd_sqr(dd a) {
   e = e + 2.0 * a.hi * a.lo;
   return fast_two_sum(p, e);
 }
-__device__ __forceinline__ dd shfl_xor_dd(dd v, int d) {
-  return {__shfl_xor(v.hi, d, 64), __shfl_xor(v.lo, d, 64)};
+
+// ---------------------------------------------------------------- moments
+// Sums of non-negative terms as unnormalised double-double pairs: the high
+// parts add error-free (two_sum), the low parts collect the rounding errors
+// in plain fp64. With no cancellation the relative error stays near 2^-100,
+// far below the single rounding to fp64 that the mean and the variance take.
+struct sd {
+  double hi, lo;
+};
+__device__ __forceinline__ sd sd_add(sd a, sd b) {
+  const dd s = two_sum(a.hi, b.hi);
+  return {s.hi, (a.lo + b.lo) + s.lo};
 }
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_move<CTRL>((uint32_t)u), hi = dpp_move<CTRL>((uint32_t)(u >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ void sd_scan_step(sd& a, sd& b, bool take) {
+  const sd ta{dpp_f64<CTRL>(a.hi), dpp_f64<CTRL>(a.lo)};
+  const sd tb{dpp_f64<CTRL>(b.hi), dpp_f64<CTRL>(b.lo)};
+  if (take) {
+    a = sd_add(a, ta);
+    b = sd_add(b, tb);
+  }
+}
+// Wavefront totals of two pair sums in every lane (the inclusive scan's lane
+// 63). Needs all 64 lanes active.
+__device__ __forceinline__ void wave_sum_sd(sd& a, sd& b) {
+  const uint32_t lane = threadIdx.x & 63u, rl = lane & 15u;
+  sd_scan_step<0x111>(a, b, rl >= 1u);  // row_shr:1
+  sd_scan_step<0x112>(a, b, rl >= 2u);  // row_shr:2
+  sd_scan_step<0x114>(a, b, rl >= 4u);  // row_shr:4
+  sd_scan_step<0x118>(a, b, rl >= 8u);  // row_shr:8
+  sd_scan_step<0x142>(a, b, (lane & 31u) >= 16u);  // row_bcast:15
+  sd_scan_step<0x143>(a, b, lane >= 32u);          // row_bcast:31
+  a = {readlane_f64(a.hi, 63), readlane_f64(a.lo, 63)};
+  b = {readlane_f64(b.hi, 63), readlane_f64(b.lo, 63)};
+}
+
+// Totals of two pair sums over lanes 0..15 (the first row's inclusive scan,
+// read back from lane 15 to every lane). Needs all 64 lanes active.
+__device__ __forceinline__ void row0_sum_sd(sd& a, sd& b) {
+  const uint32_t rl = threadIdx.x & 15u;
+  sd_scan_step<0x111>(a, b, rl >= 1u);  // row_shr:1
+  sd_scan_step<0x112>(a, b, rl >= 2u);  // row_shr:2
+  sd_scan_step<0x114>(a, b, rl >= 4u);  // row_shr:4
+  sd_scan_step<0x118>(a, b, rl >= 8u);  // row_shr:8
+  a = {readlane_f64(a.hi, 15), readlane_f64(a.lo, 15)};
+  b = {readlane_f64(b.hi, 15), readlane_f64(b.lo, 15)};
+}
+
+// Sums of a thread's E scores (keys) and of their squares. A power-of-two
+// offset sigma >= E * (largest score) goes in first: every running sum then
+// lies in [sigma, 2 sigma), at or above each addend, so Fast2Sum yields each
+// rounding error exactly, and taking sigma out at the end is exact
+// (Sterbenz). Squares of fp32 values are exact in fp64. Keys of 0 add
+// nothing.
+template <int E>
+__device__ __forceinline__ void thread_moments(const uint32_t (&key)[E], uint32_t kmax, sd& S1, sd& S2) {
+  constexpr int LE = E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1));  // ceil(log2 E)
+  const int eb = max((int)(kmax >> 23), 1);  // largest score < 2^(eb - 126), its square < 2^(2 eb - 252)
+  const double sig1 = __longlong_as_double((long long)(eb - 126 + LE + 1023) << 52);
+  const double sig2 = __longlong_as_double((long long)(2 * eb - 252 + LE + 1023) << 52);
+  double a1 = sig1, e1 = 0.0, a2 = sig2, e2 = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double s = (double)__uint_as_float(key[e]);
+    const double t1 = a1 + s;
+    e1 += s - (t1 - a1);
+    a1 = t1;
+    const double q = s * s;
+    const double t2 = a2 + q;
+    e2 += q - (t2 - a2);
+    a2 = t2;
+  }
+  S1 = {a1 - sig1, e1};
+  S2 = {a2 - sig2, e2};
+}
+
+// Moment parts published by other workgroups of the same launch (fused
+// forward). parts == nullptr: the gate workgroup sums its own scores, as it
+// also does when the parts are not all in after wait_ticks.
+struct PartsIn {
+  const sl::MomentPart* parts = nullptr;
+  int count = 0;            // parts expected (slices of 64 inputs)
+  uint32_t tag = 0;         // tag of this launch's parts
+  uint32_t wait_ticks = 0;  // s_memrealtime ticks (100 MHz) before the gate sums its own scores
+};
 
 // Threshold t (>= 0 keeps score > t; < 0 keeps everything) as a key pair.
 __device__ __forceinline__ void thresh_to_key(double t, int n, uint32_t& kthr, int& jlast) {
@@ -230,8 +332,9 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
                                           uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
                                           double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
                                           uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
-                                          uint32_t* res, uint64_t* cand, dd (*dsum)[2],
-                                          uint32_t (*kminmax)[2], int b, uint32_t& kthr_out, int& jlast_out) {
+                                          uint32_t* res, uint64_t* cand, sd (*dsum)[2],
+                                          uint32_t (*kminmax)[2], int b, PartsIn pin, uint32_t& kthr_out,
+                                          int& jlast_out) {
   constexpr int E = 4 * G;
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const XT* xb = x + (size_t)b * n;
@@ -395,68 +498,122 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
     }
   } else {
     if constexpr (MODE == MODE_STAT) {
-      // per-thread cascaded sums of s and s^2 (s^2 of an fp32 value is exact in fp64)
-      double a1 = 0.0, e1 = 0.0, a2 = 0.0, e2 = 0.0;
+      sd S1{0.0, 0.0}, S2{0.0, 0.0};
       uint32_t kmin = 0xffffffffu, kmax = 0u;
+      const dd inv_n = dd_recip((double)n);  // early: its divisions stay off the final chain
+      bool local = pin.parts == nullptr;
+      if (!local) {
+        // parts of every 64-input slice, part q in lane q mod 64 of
+        // wavefront q / 64: each such wavefront polls until all of its parts
+        // carry this launch's tag, sums them over its lanes, and the
+        // wavefront totals meet in LDS
+        const int nw = (pin.count + 63) >> 6;  // <= GW: n <= 32768
+        const int q = 64 * w + lane;
+        const bool have = q < pin.count;
+        bool all = false;
+        if (w < nw) {
+          // one round trip per poll: every word of the lane's part, each
+          // carrying the writer's tag
+          const uint64_t* pq = pin.parts[have ? q : 0].w;
+          const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + pin.wait_ticks;
+          uint32_t v[sl::kMomentWords];
+          for (;;) {
+            bool in = true;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        if (index(e) < n) {
-          const double s = (double)__uint_as_float(key[e]);
-          dd p = two_sum(a1, s);
-          a1 = p.hi;
-          e1 = e1 + p.lo;
-          p = two_sum(a2, s * s);
-          a2 = p.hi;
-          e2 = e2 + p.lo;
-          kmin = min(kmin, key[e]);
-          kmax = max(kmax, key[e]);
+            for (int k = 0; k < sl::kMomentWords; ++k) {
+              const uint64_t u = have ? __hip_atomic_load(pq + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : ((uint64_t)pin.tag << 32) | (k == 8 ? 0xffffffffull : 0ull);
+              v[k] = (uint32_t)u;
+              in &= (uint32_t)(u >> 32) == pin.tag;
+            }
+            all = __ballot(!in) == 0ull;
+            if (all || __builtin_amdgcn_s_memrealtime() > t_end) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
+          auto dbl = [&](int k) {
+            return __longlong_as_double((long long)(((uint64_t)v[k + 1] << 32) | v[k]));
+          };
+          S1 = sd{dbl(0), dbl(2)};
+          S2 = sd{dbl(4), dbl(6)};
+          wave_sum_sd(S1, S2);
+          kmin = ~wave_max(~v[8]);
+          kmax = wave_max(v[9]);
+          if (lane == 0) {
+            wsum[w] = all ? 1u : 0u;
+            dsum[w][0] = S1;
+            dsum[w][1] = S2;
+            kminmax[w][0] = kmin;
+            kminmax[w][1] = kmax;
+          }
         }
+        __syncthreads();
+        all = true;
+        for (int k = 0; k < nw; ++k) all &= wsum[k] != 0u;
+        if (all && w == 0) {
+          S1 = lane < nw ? dsum[lane][0] : sd{0.0, 0.0};
+          S2 = lane < nw ? dsum[lane][1] : sd{0.0, 0.0};
+          kmin = lane < nw ? kminmax[lane][0] : 0xffffffffu;
+          kmax = lane < nw ? kminmax[lane][1] : 0u;
+        }
+        local = !all;
       }
-      dd S1 = fast_two_sum(a1, e1), S2 = fast_two_sum(a2, e2);
+      if (local) {
+        // this workgroup's scores: per-thread sums, per-wavefront totals,
+        // then the 16 wavefront totals in wavefront 0
+        uint32_t kall = 0u;
+        kmin = 0xffffffffu;
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) {
-        S1 = dd_add(S1, shfl_xor_dd(S1, d));
-        S2 = dd_add(S2, shfl_xor_dd(S2, d));
-      }
-      kmax = wave_max(kmax);
-      kmin = ~wave_max(~kmin);
-      if (lane == 0) {
-        dsum[w][0] = S1;
-        dsum[w][1] = S2;
-        kminmax[w][0] = kmin;
-        kminmax[w][1] = kmax;
-      }
-      __syncthreads();
-      if (t == 0) {
-        dd T1 = dsum[0][0], T2 = dsum[0][1];
-        uint32_t lo = kminmax[0][0], hi = kminmax[0][1];
-        for (int k = 1; k < GW; ++k) {
-          T1 = dd_add(T1, dsum[k][0]);
-          T2 = dd_add(T2, dsum[k][1]);
-          lo = min(lo, kminmax[k][0]);
-          hi = max(hi, kminmax[k][1]);
+        for (int e = 0; e < E; ++e) {
+          kall = max(kall, key[e]);  // padding keys are 0
+          if (index(e) < n) kmin = min(kmin, key[e]);
         }
-        const double nd = (double)n;
-        const dd mu = dd_div(T1, nd);
-        double var;
-        double mean = mu.hi;
-        if (lo == hi) {  // all scores equal: exact mean, zero variance
-          mean = (double)__uint_as_float(lo);
-          var = 0.0;
-        } else {
-          const dd ex2 = dd_div(T2, nd);
-          const dd msq = dd_sqr(mu);
-          const dd v = dd_add(ex2, dd{-msq.hi, -msq.lo});
-          var = v.hi > 0.0 ? v.hi : 0.0;
+        kmax = kall;
+        thread_moments<E>(key, kall, S1, S2);
+        wave_sum_sd(S1, S2);
+        kmax = wave_max(kmax);
+        kmin = ~wave_max(~kmin);
+        if (lane == 0) {
+          dsum[w][0] = S1;
+          dsum[w][1] = S2;
+          kminmax[w][0] = kmin;
+          kminmax[w][1] = kmax;
         }
-        const double sigma = sqrt(var);
-        const double tt = __dadd_rn(mean, __dmul_rn(sigma, z));
-        uint32_t kt;
-        int jl;
-        thresh_to_key(tt, n, kt, jl);
-        res[0] = kt;
-        res[1] = (uint32_t)jl;
-        dsum[0][0].hi = tt;
+        __syncthreads();
+        if (w == 0) {
+          S1 = lane < GW ? dsum[lane][0] : sd{0.0, 0.0};
+          S2 = lane < GW ? dsum[lane][1] : sd{0.0, 0.0};
+          kmin = lane < GW ? kminmax[lane][0] : 0xffffffffu;
+          kmax = lane < GW ? kminmax[lane][1] : 0u;
+        }
+      }
+      if (w == 0) {
+        // the wavefront totals sit in lanes 0..15 (nothing above)
+        row0_sum_sd(S1, S2);
+        kmax = wave_max(kmax);
+        kmin = ~wave_max(~kmin);
+        if (lane == 0) {
+          const dd T1 = fast_two_sum(S1.hi, S1.lo), T2 = fast_two_sum(S2.hi, S2.lo);
+          const dd mu = dd_mul(T1, inv_n);
+          double var;
+          double mean = mu.hi;
+          if (kmin == kmax) {  // all scores equal: exact mean, zero variance
+            mean = (double)__uint_as_float(kmin);
+            var = 0.0;
+          } else {
+            const dd ex2 = dd_mul(T2, inv_n);
+            const dd msq = dd_sqr(mu);
+            const dd v = dd_add(ex2, dd{-msq.hi, -msq.lo});
+            var = v.hi > 0.0 ? v.hi : 0.0;
+          }
+          const double sigma = sqrt(var);
+          const double tt = __dadd_rn(mean, __dmul_rn(sigma, z));
+          uint32_t kt;
+          int jl;
+          thresh_to_key(tt, n, kt, jl);
+          res[0] = kt;
+          res[1] = (uint32_t)jl;
+          dsum[0][0].hi = tt;
+        }
       }
       __syncthreads();
       kthr = res[0];

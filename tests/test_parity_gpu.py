@@ -164,17 +164,49 @@ def test_stat_gate_small(fas, s_keep):
     layer.close()
 
 
-def test_stat_gate_constant_scores(fas):
+@pytest.mark.parametrize("dtype,fused", [("f32", False), ("bf16", False), ("bf16", True)])
+def test_stat_gate_constant_scores(fas, dtype, fused):
     # every score equal: sigma = 0, t = mu, nothing kept, y = 0
     m, n = 64, 500
-    W = wl.random_matrix(6, m, n, "f32")
+    W = wl.random_matrix(6, m, n, dtype)
     c = np.ones(n, np.float32)
     layer = _layer(fas, W, c, "stat", s_keep=0.1)
+    layer.set_fused(fused)
     x = np.full(n, -0.75, np.float32)
+    if dtype == "bf16":
+        x = wl.f32_to_bf16_bits(x)
     out = _fwd(layer, x)
     check_token(out, 0, W, c, x, "stat", s_keep=0.1, ctx="stat-constant")
     assert int(out["count"][0]) == 0 and float(out["thresh"][0]) == 0.75
     assert torch.count_nonzero(out["y"]).item() == 0
+
+
+def test_stat_fused_plans(fas):
+    """Fused statistical gate under every launch shape: the moment sums come
+    from parts that one wavefront per 64-input slice publishes (row tiles
+    fewer or more than the slices of a chunk), or, when the launch has more
+    workgroups than the device holds at once, from the gate workgroup's own
+    scores. Masks, counts and thresholds equal the oracle's and the two-launch
+    path's."""
+    m, n = 2048, 5000
+    W = wl.random_matrix(130, m, n, "bf16")
+    c = oracle.column_norms(W)
+    layer = _layer(fas, W, c, "stat", s_keep=0.15)
+    xs = [wl.random_tokens(131 + t, 1, n, "bf16", kind)[0] for t, kind in enumerate(["laplace", "normal", "ties"])]
+    layer.set_fused(False)
+    ref = [{k: v.clone() for k, v in _fwd(layer, x).items()} for x in xs]
+    layer.set_fused(True)
+    rows = np.arange(0, m, 29)
+    for rpt in (128, 256, 512):
+        for splits in (1, 5, 64, 150):
+            layer.set_plan(rpt, splits)
+            for t, x in enumerate(xs):
+                print(f"[stat plan] rows {rpt} splits {splits} token {t}", flush=True)
+                out = _fwd(layer, x)
+                for k in ("mask", "count", "thresh"):
+                    assert torch.equal(out[k], ref[t][k]), (rpt, splits, t, k)
+                check_token(out, 0, W, c, x, "stat", s_keep=0.15, rows=rows, ctx=f"stat plan {rpt}/{splits}")
+    layer.close()
 
 
 @pytest.mark.parametrize("tau", [0.0, 0.01, 0.05, 1e9])
