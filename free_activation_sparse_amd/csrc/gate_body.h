@@ -349,13 +349,18 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
     for (int e = 0; e < 4; ++e) key[g * 4 + e] = k4[e];
   }
 
-  // the product that follows adds its split partials into y atomically;
-  // device-coherent stores, so that product workgroups of the same launch on
-  // other XCDs add onto the zeros
-  if (zero_y != nullptr) {
-    float* yb = zero_y + (size_t)b * m;
-    for (int i = t; i < m; i += GT) __hip_atomic_store(yb + i, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  // The product that follows adds its split partials into y atomically, so
+  // y is cleared here with device-coherent stores (product workgroups of the
+  // same launch on other XCDs add onto the zeros). They are issued by
+  // wavefronts w_lo.. while wavefront 0 works alone (bin search, final
+  // scalar steps): issued beside the input loads they delayed those.
+  auto clear_y = [&](int w_lo) {
+    if (zero_y != nullptr && w >= w_lo) {
+      float* yb = zero_y + (size_t)b * m;
+      for (int i = t - 64 * w_lo; i < m; i += GT - 64 * w_lo)
+        __hip_atomic_store(yb + i, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
 
   uint32_t kthr = 0xffffffffu;
   int jlast = -1;
@@ -365,6 +370,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
   if constexpr (MODE == MODE_TOPK) {
     count = K;
     if (K == 0) {
+      clear_y(0);
       thresh = __longlong_as_double(0x7ff0000000000000ll);  // +inf: nothing kept
     } else {
       for (int i = t; i < 4096; i += GT) h1[i] = 0u;
@@ -393,7 +399,10 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       }
       __syncthreads();
       // fewer reads in flight when the keys take many registers
-      if (w == 0) find_bin_wave<4096, (E <= 16 ? 8 : 2)>(h1, (uint32_t)K, res);
+      if (w == 0)
+        find_bin_wave<4096, (E <= 16 ? 8 : 2)>(h1, (uint32_t)K, res);
+      else
+        clear_y(1);
       __syncthreads();
       const bool in_window = res[0] != 0xffffffffu;
       const uint32_t c1 = in_window ? res[2] : 0u;
@@ -586,6 +595,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           kmax = lane < GW ? kminmax[lane][1] : 0u;
         }
       }
+      clear_y(1);
       if (w == 0) {
         // the wavefront totals sit in lanes 0..15 (nothing above)
         row0_sum_sd(S1, S2);
@@ -620,6 +630,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       jlast = (int)res[1];
       thresh = dsum[0][0].hi;
     } else {  // MODE_FIXED
+      clear_y(0);
       thresh = (double)tau;
       thresh_to_key(thresh, n, kthr, jlast);
     }
