@@ -135,8 +135,9 @@ sl::Plan make_plan(const sl_linear* h, bool dense, sl_dtype ydt) {
   return p;
 }
 
-// Union (B > 1) product: 128-row tiles; input chunks of 256..512 so that about
-// 1536 workgroups are in flight.
+// Union (B > 1) product: 256-row tiles; input chunks of 256..512 sized so that
+// the workgroups fill the device's slots once (a second, partial wave of
+// workgroups cost ~20 % on the Qwen-shaped layers).
 int max_union_splits(int64_t n) { return (int)std::max<int64_t>(1, (n + sl::kUnionMinChunk - 1) / sl::kUnionMinChunk); }
 
 sl::UnionPlan make_union_plan(const sl_linear* h, sl_dtype ydt) {
@@ -145,7 +146,8 @@ sl::UnionPlan make_union_plan(const sl_linear* h, sl_dtype ydt) {
   p.rows = (h->uplan_rows == 128 || h->uplan_rows == 256) ? h->uplan_rows : 256;
   p.tiles = (int)((h->m + p.rows - 1) / p.rows);
   const int64_t n = h->n;
-  int splits = (int)std::max<int64_t>(1, (h->uplan_wgs > 0 ? h->uplan_wgs : 1024) / p.tiles);
+  const int slots = std::max(1, h->cus) * sl::union_workgroups_per_cu(p.rows, ydt, p.atomic);
+  int splits = (int)std::max<int64_t>(1, (h->uplan_wgs > 0 ? h->uplan_wgs : slots) / p.tiles);
   splits = std::min(splits, max_union_splits(n));
   splits = std::max<int>(splits, (int)((n + sl::kUnionMaxChunk - 1) / sl::kUnionMaxChunk));
   p.chunk = (int)((n + splits - 1) / splits);

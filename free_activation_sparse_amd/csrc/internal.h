@@ -129,6 +129,8 @@ hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, cons
 bool fused_supported(const sl_linear* h, const void* x);
 hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
                         double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s);
+// Union-product workgroups resident per compute unit (occupancy query).
+int union_workgroups_per_cu(int rows, sl_dtype ydt, bool atomic);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,
                                 bool dense, void* y, sl_dtype ydt, hipStream_t s);
 

@@ -32,6 +32,8 @@
 #include "device_common.h"
 #include "internal.h"
 
+#include <algorithm>
+
 namespace {
 
 using namespace sl::dev;
@@ -89,19 +91,14 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   const int row0 = tile * UR;
   constexpr int ROUNDS = sl::kUnionMaxChunk / UT;
 
-  if (t < 16) {
-    gk[t] = (t < B && !dense) ? gout[t].kthr : 0u;
-    gj[t] = (t < B && !dense) ? gout[t].jlast : 0;
-  }
-  __syncthreads();
-
   // 1. union of the B kept sets over this chunk, and the X_U tile
   const int nr = (j1 - j0 + UT - 1) / UT;
   uint32_t tmask[ROUNDS];
   uint64_t bal[ROUNDS];
   uint16_t xr[ROUNDS][16];
   // all loads unconditional (token and input indices clamped) so they are in
-  // flight together; values of tokens >= B are masked out below
+  // flight together, and issued before the wait for the gate pairs; values of
+  // tokens >= B are masked out below
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * UT + t;
@@ -109,6 +106,11 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int b = 0; b < 16; ++b) xr[q][b] = x[(size_t)(b < B ? b : B - 1) * n + jc];
   }
+  if (t < 16) {
+    gk[t] = (t < B && !dense) ? gout[t].kthr : 0u;
+    gj[t] = (t < B && !dense) ? gout[t].jlast : 0;
+  }
+  __syncthreads();
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * UT + t;
@@ -283,6 +285,21 @@ hipError_t go_nd(const sl_linear* h, const sl::UnionPlan& p, const void* x, int 
   return hipGetLastError();
 }
 
+template <typename YT, bool ATOMIC, int NB, int D>
+int per_cu_nd() {
+  static const int nb = [] {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, union_kernel<YT, ATOMIC, NB, D>, UT, 0) != hipSuccess) v = 1;
+    return std::max(1, v);
+  }();
+  return nb;
+}
+
+template <typename YT, bool ATOMIC>
+int per_cu(int rows) {
+  return rows == 256 ? per_cu_nd<YT, ATOMIC, 4, 3>() : per_cu_nd<YT, ATOMIC, 2, 4>();
+}
+
 template <typename YT, bool ATOMIC>
 hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
               hipStream_t s) {
@@ -293,6 +310,12 @@ hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, 
 }  // namespace
 
 namespace sl {
+
+int union_workgroups_per_cu(int rows, sl_dtype ydt, bool atomic) {
+  if (ydt == SL_BF16) return per_cu<uint16_t, false>(rows);
+  if (atomic) return per_cu<float, true>(rows);
+  return per_cu<float, false>(rows);
+}
 
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B, bool dense, void* y,
                                 sl_dtype ydt, hipStream_t s) {
