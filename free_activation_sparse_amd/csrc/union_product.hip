@@ -79,8 +79,6 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   __shared__ __align__(16) uint8_t xu[16 * XPITCH];        // X_U, [token][k] bf16
   __shared__ uint16_t ulist[sl::kUnionMaxChunk + UK];      // union columns, offsets from j0
   __shared__ uint32_t wcnt[sl::kUnionMaxChunk / UT][4];
-  __shared__ uint32_t gk[16];
-  __shared__ int gj[16];
   __shared__ uint32_t s_last;
 
   const int tile = blockIdx.x % tiles;
@@ -106,11 +104,19 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int b = 0; b < 16; ++b) xr[q][b] = x[(size_t)(b < B ? b : B - 1) * n + jc];
   }
-  if (t < 16) {
-    gk[t] = (t < B && !dense) ? gout[t].kthr : 0u;
-    gj[t] = (t < B && !dense) ? gout[t].jlast : 0;
+  // the B gate pairs as scalars (uniform loads, in flight with the x loads);
+  // tokens >= B keep nothing, the dense product keeps everything
+  uint32_t gk[16];
+  int gj[16];
+  // (unconditional loads from a clamped index: all in flight together)
+  const uint64_t* gp = (const uint64_t*)gout;  // GateOut: kthr, jlast first
+#pragma unroll
+  for (int b = 0; b < 16; ++b) {
+    const uint64_t g = gp[(size_t)(b < B ? b : 0) * (sizeof(sl::GateOut) / 8)];
+    const bool tok = b < B;
+    gk[b] = !tok ? 0xffffffffu : dense ? 0u : (uint32_t)g;
+    gj[b] = !tok ? -1 : dense ? n : (int)(uint32_t)(g >> 32);
   }
-  __syncthreads();
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * UT + t;
@@ -120,8 +126,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
       const float xv = __uint_as_float((uint32_t)xr[q][b] << 16);
-      const bool keep = b < B && (dense || gate_keep(score_key(xv, cv), jc, gk[b], gj[b]));
-      mk |= keep ? (1u << b) : 0u;
+      mk |= gate_keep(score_key(xv, cv), jc, gk[b], gj[b]) ? (1u << b) : 0u;
     }
     tmask[q] = (q < nr && j < j1) ? mk : 0u;
     bal[q] = __ballot(tmask[q] != 0u);
