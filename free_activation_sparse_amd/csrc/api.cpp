@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <cmath>
 #include <new>
 #include <string>
 #include <vector>
@@ -152,7 +153,19 @@ sl::UnionPlan make_union_plan(const sl_linear* h, sl_dtype ydt) {
   splits = std::max<int>(splits, (int)((n + sl::kUnionMaxChunk - 1) / sl::kUnionMaxChunk));
   p.chunk = (int)((n + splits - 1) / splits);
   p.splits = (int)((n + p.chunk - 1) / p.chunk);
+  p.spec = false;  // set per forward from the batch size (expected union density)
   return p;
+}
+
+// Expected union density 1 - (1 - f)^B of B independent tokens keeping a
+// fraction f each; only steers the union product's speculative first loads.
+bool union_spec(const sl_linear* h, int B, bool dense) {
+  if (dense) return true;
+  double f = 0.0;
+  if (h->gate == SL_GATE_TOPK) f = h->n > 0 ? (double)h->K / (double)h->n : 0.0;
+  else if (h->gate == SL_GATE_STAT) f = h->s_keep;
+  else return false;  // fixed threshold: no prior on the kept fraction
+  return 1.0 - std::pow(1.0 - f, (double)B) >= 0.98;
 }
 
 sl_status check_device(const sl_linear* h) {
@@ -345,7 +358,11 @@ static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl
       SL_HIP(sl::launch_gate(h, x, B, mask_out, count_out, thresh_out, (zero && full) ? (float*)y : nullptr, s));
     else if (zero && full)
       SL_HIP(sl::launch_zero((float*)y, (int64_t)B * h->m, s));
-    if (stages & SL_STAGE_PRODUCT) SL_HIP(sl::launch_union_product(h, up, x, B, dense, y, y_dtype, s));
+    if (stages & SL_STAGE_PRODUCT) {
+      sl::UnionPlan ups = up;
+      ups.spec = union_spec(h, B, dense);
+      SL_HIP(sl::launch_union_product(h, ups, x, B, dense, y, y_dtype, s));
+    }
     return SL_OK;
   }
 

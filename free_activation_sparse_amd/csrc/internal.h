@@ -50,6 +50,7 @@ struct UnionPlan {
   int splits;  // input chunks
   int chunk;   // inputs per chunk (kUnionMinChunk..kUnionMaxChunk unless n is smaller)
   bool atomic; // fp32 atomic split reduction (else ordered, reproducible)
+  bool spec;   // load the first steps before the union is known, assuming a dense prefix
 };
 
 // Hand-off from the gate workgroup to the product workgroups of one fused

@@ -64,7 +64,7 @@ template <typename YT, bool ATOMIC, int NB, int D>
 __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ x,
                                                    const float* __restrict__ c,
                                                    const sl::GateOut* __restrict__ gout, int m, int n, int B,
-                                                   int tiles, int splits, int chunk, bool dense,
+                                                   int tiles, int splits, int chunk, bool dense, bool spec,
                                                    float* __restrict__ partials, uint32_t* __restrict__ ctr,
                                                    YT* __restrict__ y) {
   constexpr int UR = 64 * NB;          // rows per tile
@@ -94,15 +94,69 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   uint32_t tmask[ROUNDS];
   uint64_t bal[ROUNDS];
   uint16_t xr[ROUNDS][16];
+  float cr[ROUNDS];
   // all loads unconditional (token and input indices clamped) so they are in
-  // flight together, and issued before the wait for the gate pairs; values of
-  // tokens >= B are masked out below
+  // flight together, and issued before any weight load (vector loads complete
+  // in order); values of tokens >= B are masked out below
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * UT + t;
     const int jc = j < j1 ? j : j1 - 1;
 #pragma unroll
     for (int b = 0; b < 16; ++b) xr[q][b] = x[(size_t)(b < B ? b : B - 1) * n + jc];
+    cr[q] = c[jc];
+  }
+  // Operand staging for step 2 (set up first: with spec the first D steps
+  // are loaded before the union is known). Thread t moves NB 16-byte vectors
+  // per step: vector v = t + UT * i covers rows 8 * (v mod R/8) .. +8 of step
+  // column v / (R/8).
+  constexpr int VPC = UR / 8;  // 16-byte vectors per column run
+  int lcol[NB], lrow[NB];
+  const uint16_t* gsrc[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int v = t + UT * i;
+    lcol[i] = v / VPC;
+    lrow[i] = (v % VPC) * 8;
+    // clamped into range; rows >= m are loaded from row m - 8 and never written
+    gsrc[i] = Wt + (size_t)j0 * m + min(row0 + lrow[i], m - 8);
+  }
+  f32x4 acc[NB];
+#pragma unroll
+  for (int h = 0; h < NB; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int rb = w * 16 * NB;  // this wavefront's rows inside the tile
+  const int ti = lane & 15;    // token (B operand column) / row within block
+  const int kg = lane >> 4;    // k group (G)
+  // transposing-read address of this lane: column 4G + ti/4 (+16 for the
+  // second half), rows rb + 4 (ti mod 4) .. +4 (+16 per block h)
+  const int aoff = (4 * kg + (ti >> 2)) * WPITCH + 2 * (rb + 4 * (ti & 3));
+  u32x4 pr[D][NB];             // ring of prefetched steps: step q lives in slot q % D
+  auto gload = [&](int slot, int q) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int col = ulist[q * UK + lcol[i]];
+      pr[slot][i] = __builtin_nontemporal_load((const u32x4*)(gsrc[i] + (size_t)col * m));
+    }
+  };
+  auto lstore = [&](int slot, int buf) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      *(u32x4*)(ws[buf] + lcol[i] * WPITCH + 2 * lrow[i]) = pr[slot][i];
+    }
+  };
+  // Speculation (near-dense unions, chosen by the host from the expected
+  // union density): the first D steps of a dense prefix, i.e. chunk columns
+  // 0 .. 32 D - 1 (clamped into the chunk), go out now; they are kept once
+  // the union turns out to start with exactly those columns.
+  if (spec) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int col = min(d * UK + lcol[i], j1 - j0 - 1);
+        pr[d][i] = __builtin_nontemporal_load((const u32x4*)(gsrc[i] + (size_t)col * m));
+      }
+    }
   }
   // the B gate pairs as scalars (uniform loads, in flight with the x loads);
   // tokens >= B keep nothing, the dense product keeps everything
@@ -121,7 +175,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   for (int q = 0; q < ROUNDS; ++q) {
     const int j = j0 + q * UT + t;
     const int jc = j < j1 ? j : j1 - 1;
-    const float cv = c[jc];
+    const float cv = cr[q];
     uint32_t mk = 0u;
 #pragma unroll
     for (int b = 0; b < 16; ++b) {
@@ -157,47 +211,16 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   }
   __syncthreads();
 
-  // 2. stream the union columns' row tiles through LDS into the MFMAs. Thread
-  //    t moves NB 16-byte vectors per step: vector v = t + UT * i covers rows
-  //    8 * (v mod R/8) .. +8 of step column v / (R/8).
-  constexpr int VPC = UR / 8;  // 16-byte vectors per column run
-  int lcol[NB], lrow[NB];
-  const uint16_t* gsrc[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int v = t + UT * i;
-    lcol[i] = v / VPC;
-    lrow[i] = (v % VPC) * 8;
-    // clamped into range; rows >= m are loaded from row m - 8 and never written
-    gsrc[i] = Wt + (size_t)j0 * m + min(row0 + lrow[i], m - 8);
-  }
-  f32x4 acc[NB];
-#pragma unroll
-  for (int h = 0; h < NB; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int rb = w * 16 * NB;  // this wavefront's rows inside the tile
-  const int ti = lane & 15;    // token (B operand column) / row within block
-  const int kg = lane >> 4;    // k group (G)
-  // transposing-read address of this lane: column 4G + ti/4 (+16 for the
-  // second half), rows rb + 4 (ti mod 4) .. +4 (+16 per block h)
-  const int aoff = (4 * kg + (ti >> 2)) * WPITCH + 2 * (rb + 4 * (ti & 3));
+  // 2. stream the union columns' row tiles through LDS into the MFMAs
   const int nsteps = cntp / UK;
-  u32x4 pr[D][NB];             // ring of prefetched steps: step q lives in slot q % D
-  auto gload = [&](int slot, int q) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int col = ulist[q * UK + lcol[i]];
-      pr[slot][i] = __builtin_nontemporal_load((const u32x4*)(gsrc[i] + (size_t)col * m));
-    }
-  };
-  auto lstore = [&](int slot, int buf) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      *(u32x4*)(ws[buf] + lcol[i] * WPITCH + 2 * lrow[i]) = pr[slot][i];
-    }
-  };
+  // the speculative loads hold iff the union's first min(cnt, 32 D) columns
+  // are chunk columns 0, 1, ... (the union list is ascending and distinct, so
+  // its last entry there decides); steps past cnt are padding (zero inputs)
+  const int L = min(cnt, D * UK);
+  const bool held = spec && (L == 0 || ulist[L - 1] == L - 1);
 #pragma unroll
   for (int d = 0; d < D; ++d)
-    if (d < nsteps) gload(d, d);
+    if (d < nsteps && !held) gload(d, d);
   if (nsteps > 0) lstore(0, 0);
   __syncthreads();
   if (D < nsteps) gload(0, D);
@@ -286,7 +309,7 @@ hipError_t go_nd(const sl_linear* h, const sl::UnionPlan& p, const void* x, int 
                  hipStream_t s) {
   union_kernel<YT, ATOMIC, NB, D><<<p.tiles * p.splits, UT, 0, s>>>(
       (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
-      p.chunk, dense, h->upartials, h->uctr, (YT*)y);
+      p.chunk, dense, p.spec, h->upartials, h->uctr, (YT*)y);
   return hipGetLastError();
 }
 
