@@ -83,6 +83,32 @@ def test_union_ragged_topk(fas, m, n, B):
         layer.close()
 
 
+def test_union_speculative_first_steps(fas):
+    """A batch whose expected union is near-dense makes the union product load
+    its first steps before the union is known, assuming each chunk starts
+    with a dense run of columns. Inputs that no token keeps (x = 0 in every
+    token at chosen columns, with K below the count of nonzero inputs) break
+    that run at different depths in different chunks: in the first, second
+    and third 32-column step of chunk 0, the last column of another chunk's
+    third step, and nowhere in the rest. Every token must still match the
+    oracle exactly in mask, count and threshold."""
+    m, n, B = 512, 4096, 16
+    W = wl.random_matrix(140, m, n, "bf16")
+    c = oracle.column_norms(W)
+    X = wl.random_tokens(141, B, n, "bf16", "laplace")
+    holes = [5, 40, 70, 512 + 95, 2048 + 33]
+    Xf = wl.bf16_bits_to_f32(X)
+    Xf[:, holes] = 0.0
+    X = wl.f32_to_bf16_bits(Xf)
+    for K in (n // 2, n - 2 * len(holes)):
+        layer = _layer(fas, W, c, "topk", 16, K=K)
+        print(f"[union speculation] K={K}", flush=True)
+        out = _fwd(layer, X)
+        _check_all(out, W, c, X, "topk", rows=np.arange(0, m, 7), ctx=f"spec K={K}", K=K)
+        assert not out["mask"][:, holes].any().item()
+        layer.close()
+
+
 @pytest.mark.parametrize("det", [False, True])
 def test_union_reduction_modes_and_bf16(fas, det):
     m, n, B = 2056, 3000, 5
