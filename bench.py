@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["sparse50", "sparse65", "dense", "all"], default="all",
+    ap.add_argument("--only", choices=["sparse50", "sparse65", "fixed50", "dense", "all"], default="all",
                     help="restrict the measured legs (short profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for memory counters)")
@@ -126,6 +126,19 @@ def main():
 
     def make_ring(K):
         return [fas.SparseLinear(Wd, c=None, gate="topk", K=K) for _ in range(RING)]
+
+    # Fixed (calibrated) threshold leg: tau = the median score over the 256
+    # tokens (c from the library; plain numpy on the host, outside any timed
+    # region), so that about half of each token's inputs are kept
+    fixed_tau, fixed_kept = None, None
+    if args.only in ("all", "fixed50"):
+        probe = fas.SparseLinear(Wd, c=None, gate="topk", K=1)
+        c_host = probe.norms().cpu().numpy().astype(np.float64)
+        probe.close()
+        xs = (wl.tokens(2, 0, 0, NTOK).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        sc = (np.abs(xs) * c_host[None, :]).astype(np.float32)
+        fixed_tau = float(np.median(sc))
+        fixed_kept = float((sc > np.float32(fixed_tau)).sum(axis=1).mean())
 
     def layer_step(ring, dense):
         """f(i, stream): forward of token i % 256 through ring copy i % 12."""
@@ -228,10 +241,14 @@ def main():
         return gate_us, prod_us, fused_us, two_us
 
     results = {}
-    legs = ["sparse50", "sparse65"] if args.only == "all" else ([args.only] if args.only != "dense" else [])
+    legs = ["sparse50", "sparse65", "fixed50"] if args.only == "all" else ([args.only] if args.only != "dense" else [])
     for leg in legs:
-        K = Ks[leg]
-        ring = make_ring(K)
+        if leg == "fixed50":
+            K = fixed_kept  # mean kept count over the tokens (algorithmic bytes)
+            ring = [fas.SparseLinear(Wd, c=None, gate="fixed", tau=fixed_tau) for _ in range(RING)]
+        else:
+            K = Ks[leg]
+            ring = make_ring(K)
         secs = run_steps(layer_step(ring, False), args.steps, args.warmup)
         gate_us, prod_us, fused_us, two_us = kernel_times(ring, False)
         for h in ring:
@@ -239,6 +256,7 @@ def main():
         ab = algorithmic_bytes(m, n, K)
         results[leg] = {
             "K": K, "sparsity": 1 - K / n,
+            **({"tau": fixed_tau, "gate": "fixed threshold (median score of the 256 tokens)"} if leg == "fixed50" else {}),
             "tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
             "fused_kernel_us": fused_us, "algorithmic_bytes": ab,
             "fused_achieved_GBps": ab / (fused_us * 1e-6) / 1e9,

@@ -374,8 +374,9 @@ static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl
   // run on its own adds onto y as it stands.
   const bool zero = plan.atomic && plan.splits > 1;
   const size_t xsz = (h->wdt == SL_BF16) ? 2 : 4;
-  if (full && gate_wanted && h->fused && sl::fused_supported(h, x)) {
-    // gate and product of each token in one launch
+  if (full && !dense && (gate_wanted || h->gate == SL_GATE_FIXED) && h->fused && sl::fused_supported(h, x)) {
+    // gate and product of each token in one launch (with a fixed threshold
+    // also when no gate output is wanted: one launch instead of fill + product)
     for (int b = 0; b < B; ++b)
       SL_HIP(sl::launch_fused(h, (const char*)x + (size_t)b * h->n * xsz, h->gout + b,
                               mask_out ? mask_out + (size_t)b * h->n : nullptr, count_out ? count_out + b : nullptr,

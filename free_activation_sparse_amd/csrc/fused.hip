@@ -68,7 +68,7 @@ __device__ __forceinline__ uint64_t pack_gate(uint32_t kthr, int jlast) {
 // the previous call.
 template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC, bool SPEC = ATOMIC>
 __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, const WT* __restrict__ x,
-                                                   const float* __restrict__ c, int m, int n, int K, double z,
+                                                   const float* __restrict__ c, int m, int n, int K, double z, float tau,
                                                    sl::GateOut* __restrict__ gout, uint8_t* __restrict__ mask_out,
                                                    int32_t* __restrict__ count_out, double* __restrict__ thresh_out,
                                                    int tiles, int splits, int chunk, float* __restrict__ partials,
@@ -88,7 +88,7 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
     const uint32_t gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sl::gatedev::PartsIn pin{};
     if (MODE == sl::gatedev::MODE_STAT && use_parts) pin = {sync->parts, (n + 63) / 64, gen + 1u, kPartsWait};
-    sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, 0.0f, gout, mask_out, count_out, thresh_out, zy, m,
+    sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zy, m,
                                               sm.g.h1, sm.g.h2, sm.g.h3, sm.g.wsum, sm.g.res, sm.g.cand,
                                               sm.g.dsum, sm.g.kminmax, 0, pin, kthr, jlast);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
@@ -166,7 +166,17 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
   // least kSpecMargin times the previous threshold; consecutive tokens'
   // thresholds differ by a few percent, so these are almost always kept.
   uint32_t g0 = 0xffffffffu;  // no speculation
-  if (SPEC && prevk != 0u && prevk < 0x7f800000u) {
+  if (MODE == sl::gatedev::MODE_FIXED) {
+    // a fixed threshold is known now: the "speculative" set is the kept set
+    // itself (the gate's pair only confirms it and orders the adds after the
+    // clearing of y)
+    if (SPEC) {
+      uint32_t kt;
+      int jl;
+      sl::gatedev::thresh_to_key((double)tau, n, kt, jl);
+      g0 = jl >= 0 ? 0u : kt + 1u;  // keep all (jlast = n - 1) or keys > kt
+    }
+  } else if (SPEC && prevk != 0u && prevk < 0x7f800000u) {
     g0 = __float_as_uint(__uint_as_float(prevk) * kSpecMargin);
     if (g0 <= prevk) g0 = prevk + 1u;
   }
@@ -308,7 +318,7 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
   // once (the gate would otherwise wait for workgroups not yet dispatched)
   const int use_parts = 1 + (int64_t)p.tiles * p.splits <= (int64_t)std::max(1, h->cus) * per_cu ? 1 : 0;
   fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(
-      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, (int)h->m, (int)h->n, (int)h->K, h->z, g, mask, cnt,
+      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, (int)h->m, (int)h->n, (int)h->K, h->z, h->tau, g, mask, cnt,
       th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, use_parts, (YT*)y);
   return hipGetLastError();
 }
@@ -316,7 +326,9 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
 template <typename YT, int G, int MODE, bool ATOMIC>
 hipError_t go_lpc(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, int32_t* cnt,
                   double* th, void* y, hipStream_t s) {
-  int lpc = h->plan_rows > 0 ? h->plan_rows / 8 : (h->m >= 8192 ? 64 : (h->m >= 2048 ? 32 : 16));
+  // 512-row tiles (1 KB column runs) from 2048 rows up: on the 4096-row
+  // layers they beat 256-row tiles by ~3 % (fewer, longer runs per column)
+  int lpc = h->plan_rows > 0 ? h->plan_rows / 8 : (h->m >= 2048 ? 64 : 16);
   // taller row tiles when the chunk limit alone would ask for more product
   // workgroups than the device holds at once (a late tail of workgroups)
   const int64_t min_splits = (h->n + sl::kMaxChunk - 1) / sl::kMaxChunk;
@@ -334,6 +346,8 @@ hipError_t go_mode(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* m
                    double* th, void* y, hipStream_t s) {
   if (h->gate == SL_GATE_STAT)
     return go_lpc<YT, G, sl::gatedev::MODE_STAT, ATOMIC>(h, x, g, mask, cnt, th, y, s);
+  if (h->gate == SL_GATE_FIXED)
+    return go_lpc<YT, G, sl::gatedev::MODE_FIXED, ATOMIC>(h, x, g, mask, cnt, th, y, s);
   return go_lpc<YT, G, sl::gatedev::MODE_TOPK, ATOMIC>(h, x, g, mask, cnt, th, y, s);
 }
 
@@ -354,7 +368,7 @@ hipError_t go_g(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask
 namespace sl {
 
 bool fused_supported(const sl_linear* h, const void* x) {
-  return h->wdt == SL_BF16 && (h->gate == SL_GATE_TOPK || h->gate == SL_GATE_STAT) && h->n % 4 == 0 &&
+  return h->wdt == SL_BF16 && h->n % 4 == 0 &&
          ((uintptr_t)x % 8) == 0;
 }
 

@@ -125,8 +125,8 @@ hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_o
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
                           void* y, sl_dtype ydt, hipStream_t s);
-// Fused gate + product for one token (bf16 weights, top-K or statistical
-// gate, n % 4 == 0 and x 8-byte aligned: fused_supported).
+// Fused gate + product for one token (bf16 weights, any gate, n % 4 == 0 and
+// x 8-byte aligned: fused_supported).
 bool fused_supported(const sl_linear* h, const void* x);
 hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
                         double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s);

@@ -225,6 +225,34 @@ def test_fixed_threshold(fas, tau):
     layer.close()
 
 
+@pytest.mark.parametrize("det", [False, True])
+def test_fixed_threshold_fused_full_size(fas, llama_down, det):
+    """Fixed (calibrated) threshold on the Llama-2-7B down projection: the
+    fused launch, where the product workgroups stream the kept set without
+    waiting for a selection, against the oracle, with and without requested
+    outputs, for a threshold near the median score (about half kept), 0
+    (every nonzero score kept) and one above every score (y exactly 0)."""
+    W, c = llama_down
+    x0 = wl.token(2, 0, 200)
+    tau_mid = float(np.median(oracle.scores(x0, c)))
+    rows = np.random.default_rng(11).choice(W.shape[0], 64, replace=False)
+    for tau in (tau_mid, 0.0, 1e30):
+        layer = _layer(fas, W, c, "fixed", tau=tau)
+        layer.set_deterministic(det)
+        for t in range(4):
+            x = wl.token(2, 0, 200 + t)
+            print(f"[fixed fused det={det}] tau={tau:.4g} token {t}", flush=True)
+            check_token(_fwd(layer, x), 0, W, c, x, "fixed", tau=tau, rows=rows, ctx=f"fixed tau={tau:.3g}")
+            y2 = layer.forward(to_dev(x, torch)[None, :])["y"]
+            layer.sync_status()
+            ref = oracle.forward(W, c, x, "fixed", tau=tau)["y"]
+            if tau == 1e30:
+                assert torch.count_nonzero(y2).item() == 0
+            else:
+                assert rel_l2(y2[0].cpu().numpy()[rows], ref[rows]) <= REL_L2_TOL
+        layer.close()
+
+
 # ---------------------------------------------------------------- identities
 def test_topk_all_equals_dense_kernel(fas):
     m, n = 1024, 4096
