@@ -380,7 +380,11 @@ def workload_legs(name):
         ps = wl.component_sparsities(3)
         lins = [(3, li, dict(gate="topk", K=wl.k_from_sparsity(l.n, round(ps[li], 6))))
                 for li, l in enumerate(wl.CONFIGS[3].linears)]
-        return [("block", 1, lins)]
+        # "grouped": the linears that share an input in one launch each
+        # (q, k, v | o | gate, up | down: 4 launches instead of 7)
+        names = [l.name for l in wl.CONFIGS[3].linears]
+        groups = [[names.index(a) for a in g] for g in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))]
+        return [("block", 1, lins), ("grouped", 1, lins, groups)]
     if name == "phi4_ffn_stat":
         lins = [(4, li, dict(gate="stat", s_keep=0.10)) for li in range(3)]
         return [(f"B{b}", b, lins) for b in (1, 2, 4, 8)]
@@ -411,7 +415,9 @@ def run_workload(args):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     results = {}
-    for leg, B, lins in legs:
+    for spec in legs:
+        leg, B, lins = spec[:3]
+        groups = spec[3] if len(spec) > 3 else None
         total = sum(wl.CONFIGS[cfg].linears[li].m * wl.CONFIGS[cfg].linears[li].n * 2 for cfg, li, _ in lins)
         R = max(2, -(-(1 << 30) // total))
         rings, Xs, Ys, dims = [], [], [], []
@@ -428,6 +434,12 @@ def run_workload(args):
             dims.append((lin.name, lin.m, lin.n))
 
         def step(i, s, stages=3):
+            if groups is not None:
+                # one token: a group's linears share x (the token of its first linear)
+                for g in groups:
+                    fas.sparse_linear_forward_group([rings[L][i % R].handle for L in g], Xs[g[0]][i % NT].data_ptr(),
+                                                    [Ys[L][i % R].data_ptr() for L in g], fas.SL_F32, s.cuda_stream)
+                return
             for L in range(len(lins)):
                 h = rings[L][i % R]
                 fas.sparse_linear_forward_stages(h.handle, Xs[L][i % NT].data_ptr(), B, Ys[L][i % R].data_ptr(),

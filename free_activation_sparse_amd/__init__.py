@@ -30,6 +30,7 @@ EXPORTED = [
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
+    "sparse_linear_forward_group",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_forward.restype = ctypes.c_int
     L.sparse_linear_forward_dense.argtypes = [_vp, _vp, _i32, _vp, ctypes.c_int, _vp]
     L.sparse_linear_forward_dense.restype = ctypes.c_int
+    L.sparse_linear_forward_group.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _vp]
+    L.sparse_linear_forward_group.restype = ctypes.c_int
     L.sparse_linear_get_norms.argtypes = [_vp, _vp, _vp]
     L.sparse_linear_get_norms.restype = ctypes.c_int
     L.sparse_linear_destroy.argtypes = [_vp]
@@ -104,6 +107,16 @@ def sparse_linear_forward(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, 
                           count_ptr: int = 0, thresh_ptr: int = 0, stream: int = 0) -> None:
     _check(lib().sparse_linear_forward(h, x_ptr, B, y_ptr, y_dtype, mask_ptr or None, count_ptr or None,
                                        thresh_ptr or None, stream or None), "sparse_linear_forward")
+
+
+def sparse_linear_forward_group(handles, x_ptr: int, y_ptrs, y_dtype: int, stream: int = 0) -> None:
+    """One token through len(handles) linears that share x (handles and
+    y_ptrs: sequences of ints)."""
+    count = len(handles)
+    ha = (_vp * max(1, count))(*handles)
+    ya = (_vp * max(1, count))(*y_ptrs)
+    _check(lib().sparse_linear_forward_group(ha, count, x_ptr, ya, y_dtype, stream or None),
+           "sparse_linear_forward_group")
 
 
 def sparse_linear_forward_dense(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, stream: int = 0) -> None:
@@ -220,6 +233,18 @@ class SparseLinear:
                               ct.data_ptr() if ct is not None else 0,
                               th.data_ptr() if th is not None else 0, self._stream())
         return {"y": y, "mask": mk, "count": ct, "thresh": th}
+
+    @staticmethod
+    def forward_group(layers, x, ys=None, y_dtype=None):
+        """y_l = layers[l](x) for one token x shared by every layer (same n and
+        dtype), in one launch where possible; returns the list of y."""
+        torch = layers[0]._torch
+        y_dtype = torch.float32 if y_dtype is None else y_dtype
+        if ys is None:
+            ys = [torch.empty((l.m,), dtype=y_dtype, device=l.device) for l in layers]
+        sparse_linear_forward_group([l.handle for l in layers], x.data_ptr(), [y.data_ptr() for y in ys],
+                                    SL_BF16 if ys[0].dtype == torch.bfloat16 else SL_F32, layers[0]._stream())
+        return ys
 
     def forward_dense(self, x, y=None, y_dtype=None):
         torch = self._torch

@@ -405,6 +405,47 @@ sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, 
   }
 }
 
+sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, const void* x, void* const* ys,
+                                      sl_dtype y_dtype, void* stream) {
+  try {
+    g_last_error.clear();
+    if (handles == nullptr || ys == nullptr || x == nullptr) return fail(SL_ERR_ARG, "NULL argument");
+    if (count < 1 || count > sl::kMaxGroupLinears)
+      return fail(SL_ERR_ARG, "count=%d outside [1, %d]", (int)count, sl::kMaxGroupLinears);
+    if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
+    for (int l = 0; l < count; ++l) {
+      const sl_linear* h = handles[l];
+      if (h == nullptr || ys[l] == nullptr) return fail(SL_ERR_ARG, "handle or y %d is NULL", l);
+      if (h->n != handles[0]->n || h->wdt != handles[0]->wdt)
+        return fail(SL_ERR_ARG, "linear %d: n or weight dtype differs from linear 0", l);
+      sl_status st = check_device(h);
+      if (st != SL_OK) return st;
+    }
+    bool grouped = count > 1 && y_dtype == SL_F32;
+    for (int l = 0; l < count && grouped; ++l) {
+      const sl_linear* h = handles[l];
+      grouped = h->fused && !h->deterministic && h->gate == handles[0]->gate && sl::fused_supported(h, x);
+    }
+    if (!grouped) {
+      for (int l = 0; l < count; ++l) {
+        sl_status st = forward_impl(handles[l], x, 1, ys[l], y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
+        if (st != SL_OK) return st;
+      }
+      return SL_OK;
+    }
+    const sl_linear* hs[sl::kMaxGroupLinears];
+    float* yf[sl::kMaxGroupLinears];
+    for (int l = 0; l < count; ++l) {
+      hs[l] = handles[l];
+      yf[l] = (float*)ys[l];
+    }
+    SL_HIP(sl::launch_fused_group(hs, count, x, yf, (hipStream_t)stream));
+    return SL_OK;
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_group");
+  }
+}
+
 sl_status sparse_linear_forward_dense(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                       void* stream) {
   try {

@@ -63,32 +63,55 @@ __device__ __forceinline__ uint64_t pack_gate(uint32_t kthr, int jlast) {
   return ((uint64_t)(uint32_t)(jlast + 2) << 32) | (uint64_t)kthr;
 }
 
-// SPEC (speculation) only with the atomic reduction, whose summation order
-// varies anyway: with the ordered reduction the result must not depend on
-// the previous call.
-template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC, bool SPEC = ATOMIC>
-__global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, const WT* __restrict__ x,
-                                                   const float* __restrict__ c, int m, int n, int K, double z, float tau,
-                                                   sl::GateOut* __restrict__ gout, uint8_t* __restrict__ mask_out,
-                                                   int32_t* __restrict__ count_out, double* __restrict__ thresh_out,
-                                                   int tiles, int splits, int chunk, float* __restrict__ partials,
-                                                   uint32_t* __restrict__ ctr, sl::FusedSync* __restrict__ sync,
-                                                   int use_parts, YT* __restrict__ y) {
-  __shared__ union {
-    GateSmem g;
-    ProdSmem<WT> p;
-  } sm;
+// One linear's share of a launch: its weights, gate and hand-off state,
+// launch shape and output (a grouped launch carries several).
+template <typename WT, typename YT>
+struct FusedArgs {
+  const WT* Wt;
+  const float* c;
+  int m, K;
+  double z;
+  float tau;
+  sl::GateOut* gout;
+  uint8_t* mask_out;
+  int32_t* count_out;
+  double* thresh_out;
+  int tiles, splits, chunk;
+  float* partials;
+  uint32_t* ctr;
+  sl::FusedSync* sync;
+  int use_parts;
+  YT* y;
+};
+
+template <typename WT>
+union FusedSmem {
+  GateSmem g;
+  ProdSmem<WT> p;
+};
+
+// The gate workgroup of one linear: selection, the pair in the flag word,
+// then the wait for every product workgroup's acknowledgement and the re-arm.
+template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC>
+__device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT* __restrict__ x, int n,
+                                           FusedSmem<WT>& sm) {
+  const float* __restrict__ c = a.c;
+  const int m = a.m, K = a.K, tiles = a.tiles, splits = a.splits, use_parts = a.use_parts;
+  const double z = a.z;
+  const float tau = a.tau;
+  sl::GateOut* __restrict__ gout = a.gout;
+  sl::FusedSync* __restrict__ sync = a.sync;
+  YT* __restrict__ y = a.y;
   const int t = threadIdx.x;
   const int nprod = tiles * splits;
-
-  if (blockIdx.x == 0) {
+  {
     uint32_t kthr;
     int jlast;
     float* zy = (ATOMIC && splits > 1) ? (float*)y : nullptr;
     const uint32_t gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sl::gatedev::PartsIn pin{};
     if (MODE == sl::gatedev::MODE_STAT && use_parts) pin = {sync->parts, (n + 63) / 64, gen + 1u, kPartsWait};
-    sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zy, m,
+    sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, tau, gout, a.mask_out, a.count_out, a.thresh_out, zy, m,
                                               sm.g.h1, sm.g.h2, sm.g.h3, sm.g.wsum, sm.g.res, sm.g.cand,
                                               sm.g.dsum, sm.g.kminmax, 0, pin, kthr, jlast);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
@@ -115,10 +138,25 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
       // under this one (late or not) no longer counts
       if (t == 0) __hip_atomic_store(&sync->gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    return;
   }
+}
 
-  const int pw = blockIdx.x - 1;
+// Product workgroup pw (0-based) of one linear. SPEC (speculation) only with
+// the atomic reduction, whose summation order varies anyway: with the ordered
+// reduction the result must not depend on the previous call.
+template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC, bool SPEC>
+__device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const WT* __restrict__ x, int n, int pw,
+                                              FusedSmem<WT>& sm) {
+  const WT* __restrict__ Wt = a.Wt;
+  const float* __restrict__ c = a.c;
+  const int m = a.m, tiles = a.tiles, splits = a.splits, chunk = a.chunk, use_parts = a.use_parts;
+  const float tau = a.tau;
+  sl::GateOut* __restrict__ gout = a.gout;
+  sl::FusedSync* __restrict__ sync = a.sync;
+  float* __restrict__ partials = a.partials;
+  uint32_t* __restrict__ ctr = a.ctr;
+  YT* __restrict__ y = a.y;
+  const int t = threadIdx.x;
   const int tile = pw % tiles;
   const int split = pw / tiles;
   const int j0 = split * chunk;
@@ -280,6 +318,44 @@ __global__ __launch_bounds__(FT) void fused_kernel(const WT* __restrict__ Wt, co
                                                    &sm.p.s_last, y);
 }
 
+// One linear: workgroup 0 is the gate, 1.. the product.
+template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC, bool SPEC = ATOMIC>
+__global__ __launch_bounds__(FT) void fused_kernel(FusedArgs<WT, YT> a, const WT* __restrict__ x, int n) {
+  __shared__ FusedSmem<WT> sm;
+  if (blockIdx.x == 0) {
+    fused_gate<WT, YT, G, MODE, LPC, ATOMIC>(a, x, n, sm);
+    return;
+  }
+  fused_product<WT, YT, G, MODE, LPC, ATOMIC, SPEC>(a, x, n, blockIdx.x - 1, sm);
+}
+
+// Grouped linears that share their input x (B = 1, fp32 y, atomic split
+// reduction): workgroups 0..count-1 are their gates, then each linear's
+// product workgroups in order (begin[l] .. begin[l + 1] - 1). Every gate
+// workgroup precedes every product workgroup in the dispatch order, as in
+// the single-linear launch.
+constexpr int kMaxGroup = sl::kMaxGroupLinears;
+template <typename WT>
+struct FusedGroup {
+  FusedArgs<WT, float> lin[kMaxGroup];
+  int begin[kMaxGroup + 1];
+  int count;
+};
+
+template <typename WT, int G, int MODE, int LPC>
+__global__ __launch_bounds__(FT) void fused_group_kernel(FusedGroup<WT> gr, const WT* __restrict__ x, int n) {
+  __shared__ FusedSmem<WT> sm;
+  const int b = blockIdx.x;
+  if (b < gr.count) {
+    fused_gate<WT, float, G, MODE, LPC, true>(gr.lin[b], x, n, sm);
+    return;
+  }
+  const int pw = b - gr.count;
+  int l = 0;
+  while (l + 1 < gr.count && pw >= gr.begin[l + 1]) ++l;  // uniform
+  fused_product<WT, float, G, MODE, LPC, true, true>(gr.lin[l], x, n, pw - gr.begin[l], sm);
+}
+
 struct FusedPlan {
   int tiles, splits, chunk;
 };
@@ -317,9 +393,10 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
   // moment parts only when every workgroup of the launch can be resident at
   // once (the gate would otherwise wait for workgroups not yet dispatched)
   const int use_parts = 1 + (int64_t)p.tiles * p.splits <= (int64_t)std::max(1, h->cus) * per_cu ? 1 : 0;
-  fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(
-      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, (int)h->m, (int)h->n, (int)h->K, h->z, h->tau, g, mask, cnt,
-      th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, use_parts, (YT*)y);
+  const FusedArgs<uint16_t, YT> a{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau, g, mask, cnt,
+                                 th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, use_parts, (YT*)y};
+  fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(a, (const uint16_t*)x,
+                                                                                          (int)h->n);
   return hipGetLastError();
 }
 
@@ -363,9 +440,91 @@ hipError_t go_g(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask
   return go_mode<YT, 8, ATOMIC>(h, x, g, mask, cnt, th, y, s);
 }
 
+// Grouped launch: every linear gets tiles x (at least) the chunk limit's
+// splits, and the remaining workgroup slots are shared in proportion to the
+// linears' expected kept bytes (m times the kept count).
+template <int G, int MODE, int LPC>
+hipError_t go_group(const sl_linear* const* hs, int count, const void* x, float* const* ys, hipStream_t s) {
+  static const int per_cu = [] {
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fused_group_kernel<uint16_t, G, MODE, LPC>, FT, 0) !=
+        hipSuccess)
+      nb = 1;
+    return std::max(1, nb);
+  }();
+  const int64_t n = hs[0]->n;
+  const int rows = LPC * 8;
+  const int64_t slots = (int64_t)std::max(1, hs[0]->cus) * per_cu - count;
+  const int64_t min_splits = (n + sl::kMaxChunk - 1) / sl::kMaxChunk;
+  const int64_t max_splits = std::min<int64_t>(sl::kMaxSplits, (n + 31) / 32);
+  double wsum = 0.0;
+  double wl[kMaxGroup];
+  int64_t tiles[kMaxGroup];
+  for (int l = 0; l < count; ++l) {
+    const sl_linear* h = hs[l];
+    const double kept = h->gate == SL_GATE_TOPK ? (double)h->K
+                        : h->gate == SL_GATE_STAT ? h->s_keep * (double)n
+                                                  : 0.5 * (double)n;
+    wl[l] = (double)h->m * std::max(1.0, kept);
+    wsum += wl[l];
+    tiles[l] = (h->m + rows - 1) / rows;
+  }
+  FusedGroup<uint16_t> gr{};
+  gr.count = count;
+  int64_t total = 0;
+  const int align = MODE == sl::gatedev::MODE_STAT ? 64 : 1;
+  for (int l = 0; l < count; ++l) {
+    const sl_linear* h = hs[l];
+    int64_t splits = (int64_t)((double)slots * wl[l] / wsum) / tiles[l];
+    splits = std::min(std::max(splits, (int64_t)1), max_splits);
+    splits = std::max(splits, min_splits);
+    int chunk = (int)((n + splits - 1) / splits);
+    chunk = (chunk + align - 1) / align * align;
+    splits = (n + chunk - 1) / chunk;
+    gr.begin[l] = (int)total;
+    gr.lin[l] = FusedArgs<uint16_t, float>{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau,
+                                           h->gout, nullptr, nullptr, nullptr, (int)tiles[l], (int)splits, chunk,
+                                           h->partials, h->ctr, h->fsync, 0, ys[l]};
+    total += tiles[l] * splits;
+  }
+  gr.begin[count] = (int)total;
+  // moment parts only when the whole grid is resident at once
+  const int use_parts = count + total <= (int64_t)std::max(1, hs[0]->cus) * per_cu ? 1 : 0;
+  for (int l = 0; l < count; ++l) gr.lin[l].use_parts = use_parts;
+  fused_group_kernel<uint16_t, G, MODE, LPC><<<(unsigned)(count + total), FT, 0, s>>>(gr, (const uint16_t*)x, (int)n);
+  return hipGetLastError();
+}
+
+template <int G, int MODE>
+hipError_t go_group_lpc(const sl_linear* const* hs, int count, const void* x, float* const* ys, hipStream_t s) {
+  int64_t mmin = hs[0]->m;
+  for (int l = 1; l < count; ++l) mmin = std::min(mmin, hs[l]->m);
+  // 512-row tiles unless a linear is shorter than two of them
+  if (mmin >= 1024) return go_group<G, MODE, 64>(hs, count, x, ys, s);
+  return go_group<G, MODE, 16>(hs, count, x, ys, s);
+}
+
+template <int G>
+hipError_t go_group_mode(const sl_linear* const* hs, int count, const void* x, float* const* ys, hipStream_t s) {
+  if (hs[0]->gate == SL_GATE_STAT) return go_group_lpc<G, sl::gatedev::MODE_STAT>(hs, count, x, ys, s);
+  if (hs[0]->gate == SL_GATE_FIXED) return go_group_lpc<G, sl::gatedev::MODE_FIXED>(hs, count, x, ys, s);
+  return go_group_lpc<G, sl::gatedev::MODE_TOPK>(hs, count, x, ys, s);
+}
+
 }  // namespace
 
 namespace sl {
+
+hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void* x, float* const* ys,
+                              hipStream_t s) {
+  const int64_t groups = (hs[0]->n + 4 * FT - 1) / (4 * FT);  // 1..8 for n <= 32768
+  if (groups <= 2) return go_group_mode<2>(hs, count, x, ys, s);
+  if (groups <= 3) return go_group_mode<3>(hs, count, x, ys, s);
+  if (groups <= 4) return go_group_mode<4>(hs, count, x, ys, s);
+  if (groups <= 5) return go_group_mode<5>(hs, count, x, ys, s);
+  if (groups <= 6) return go_group_mode<6>(hs, count, x, ys, s);
+  return go_group_mode<8>(hs, count, x, ys, s);
+}
 
 bool fused_supported(const sl_linear* h, const void* x) {
   return h->wdt == SL_BF16 && h->n % 4 == 0 &&

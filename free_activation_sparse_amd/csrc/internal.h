@@ -125,6 +125,11 @@ hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_o
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
                           void* y, sl_dtype ydt, hipStream_t s);
+// Grouped fused forward (one token) of count <= 8 linears that share x: all
+// fused_supported, the same n and gate mode, fp32 y, atomic reduction.
+constexpr int kMaxGroupLinears = 8;
+hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void* x, float* const* ys,
+                              hipStream_t s);
 // Fused gate + product for one token (bf16 weights, any gate, n % 4 == 0 and
 // x 8-byte aligned: fused_supported).
 bool fused_supported(const sl_linear* h, const void* x);

@@ -110,9 +110,9 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
  * Each token's kept set depends only on that token. For B > 1 the library
  * forms the union of the B masks and runs one matrix-core pass over the union
  * columns, feeding zero for inputs a token did not keep. A single bf16 token
- * with a top-K or statistical gate (n % 4 == 0, x 8-byte aligned) runs as one
- * fused launch: one workgroup selects while the others load their input
- * chunks, then stream the kept columns (see sparse_linear_set_fused).
+ * (n % 4 == 0, x 8-byte aligned) runs as one fused launch: one workgroup
+ * selects while the others load their input chunks, then stream the kept
+ * columns (see sparse_linear_set_fused).
  * Asynchronous on `stream`; the caller keeps x, y and the optional outputs
  * alive until the stream has completed. A handle's scratch is shared by its
  * calls, so one handle must not run on two streams at once.
@@ -120,6 +120,34 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
 sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                 uint8_t* mask_out, int32_t* count_out, double* thresh_out,
                                 void* stream);
+
+/*
+ * sparse_linear_forward_group -- one token through `count` linears that share
+ * their input x (e.g. the q, k and v projections of a decoder block, or its
+ * gate and up projections), each with its own weights, norms and gate (WINA
+ * article, section 一: per-layer K; the heterogeneous per-component sparsity
+ * of the WAS framework), in one launch: the linears' gate workgroups run side
+ * by side and the product workgroups are shared out in proportion to each
+ * linear's expected kept bytes.
+ *
+ *   handles    host array of `count` handles, 1 <= count <= 8, all on the
+ *              current device with the same n and weight dtype.
+ *   x          device [n] (one token), the weights' dtype.
+ *   ys         host array of `count` device pointers, ys[l] of [m_l] y_dtype.
+ *
+ * y_l equals sparse_linear_forward(handles[l], x, 1, ys[l], ...) up to the
+ * split reduction's summation order. The single launch is taken when every
+ * handle is bf16 with the fused forward enabled and the atomic reduction, the
+ * gates share their mode, y_dtype is fp32, n % 4 == 0 and x is 8-byte
+ * aligned; otherwise the linears run one after another. No mask, count or
+ * threshold outputs. Errors: NULL arrays or pointers, count outside 1..8,
+ * differing n or dtypes, a handle on another device (SL_ERR_ARG); nothing is
+ * launched then. Asynchronous on `stream`; the handles' scratch is in use
+ * until it completes. Timed-out hand-offs are reported per handle by
+ * sparse_linear_sync_status.
+ */
+sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, const void* x, void* const* ys,
+                                      sl_dtype y_dtype, void* stream);
 
 /*
  * sparse_linear_forward_dense -- y = W x for B tokens with every input kept,

@@ -106,6 +106,20 @@ def test_forward_rejects_null_handle_and_pointers(slib):
     assert L.sparse_linear_sync_status(None, None) == 1
 
 
+def test_forward_group_rejects_bad_arguments(slib):
+    L = slib.lib()
+    hs = (ctypes.c_void_p * 2)(None, None)
+    ys = (ctypes.c_void_p * 2)(1, 1)
+    assert L.sparse_linear_forward_group(None, 1, 1, ys, 0, None) == 1      # NULL handle array
+    assert L.sparse_linear_forward_group(hs, 1, 1, None, 0, None) == 1      # NULL y array
+    assert L.sparse_linear_forward_group(hs, 1, None, ys, 0, None) == 1     # NULL x
+    assert L.sparse_linear_forward_group(hs, 0, 1, ys, 0, None) == 1        # count < 1
+    assert L.sparse_linear_forward_group(hs, 9, 1, ys, 0, None) == 1        # count > 8
+    assert L.sparse_linear_forward_group(hs, 2, 1, ys, 0, None) == 1        # NULL handles
+    assert L.sparse_linear_forward_group(hs, 1, 1, ys, 7, None) == 1        # bad y dtype
+    assert "handle" in slib.sparse_linear_last_error() or "dtype" in slib.sparse_linear_last_error()
+
+
 def test_strerror(slib):
     assert slib.sparse_linear_strerror(0) == "success"
     assert slib.sparse_linear_strerror(2) == "unsupported shape or alignment"

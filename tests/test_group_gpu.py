@@ -1,0 +1,146 @@
+"""GPU parity of the grouped single-token forward (sparse_linear_forward_group):
+linears that share their input x (the q/k/v and gate/up projections of a
+decoder block, each with its own weights, norms and per-component K or keep
+fraction) run in one launch; every linear's y must match the oracle run on
+that linear alone (relative L2 2e-3) and the linear's own single forward up
+to summation order."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from parity_util import REL_L2_TOL, gate_kwargs, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def fas(slib):
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return slib
+
+
+def _layer(fas, W, c, mode, **g):
+    return fas.SparseLinear(to_dev(W, torch), c=to_dev(c, torch), **gate_kwargs(mode, **g))
+
+
+def _check_group(fas, layers, Ws, cs, gs, mode, x, ctx, rows_per=64):
+    xd = to_dev(x, torch)
+    ys = fas.SparseLinear.forward_group(layers, xd)
+    for l in layers:
+        l.sync_status()
+    for i, (layer, W, c, g) in enumerate(zip(layers, Ws, cs, gs)):
+        rows = np.random.default_rng(i).choice(W.shape[0], min(rows_per, W.shape[0]), replace=False)
+        ref = oracle.forward(W, c, x, mode, rows=rows, **g)
+        got = ys[i].cpu().numpy()[rows]
+        err = rel_l2(got, ref["y"])
+        if np.linalg.norm(ref["y"]) == 0:
+            assert np.count_nonzero(got) == 0, f"{ctx} linear {i}: y must be exactly 0"
+        else:
+            assert err <= REL_L2_TOL, f"{ctx} linear {i}: rel L2 {err:.3e}"
+        single = layer.forward(xd[None, :])["y"][0]
+        layer.sync_status()
+        assert rel_l2(ys[i].cpu().numpy(), single.cpu().numpy()) <= 1e-5, f"{ctx} linear {i}: vs single forward"
+    return ys
+
+
+def test_group_llama3_block_inputs(fas):
+    """q, k, v (4096, 1024, 1024 rows) and gate, up (14336 rows) of the
+    Llama-3-8B block take the same hidden state; per-component sparsity."""
+    ps = wl.component_sparsities(3)
+    lins = wl.CONFIGS[3].linears
+    idx = [li for li, l in enumerate(lins) if l.name in ("q", "k", "v", "gate", "up")]
+    Ws = [wl.weight(3, li) for li in idx]
+    cs = [oracle.column_norms(W) for W in Ws]
+    gs = [dict(K=wl.k_from_sparsity(lins[li].n, round(ps[li], 6))) for li in idx]
+    layers = [_layer(fas, W, c, "topk", **g) for W, c, g in zip(Ws, cs, gs)]
+    for t in range(3):
+        x = wl.token(3, idx[0], t)
+        for sel, name in (([0, 1, 2], "qkv"), ([3, 4], "gate/up"), ([0, 1, 2, 3, 4], "all five")):
+            print(f"[group {name}] token {t}", flush=True)
+            _check_group(fas, [layers[i] for i in sel], [Ws[i] for i in sel], [cs[i] for i in sel],
+                         [gs[i] for i in sel], "topk", x, f"{name} token {t}")
+    for l in layers:
+        l.close()
+
+
+def test_group_stat_and_fixed(fas):
+    """Statistical gate (moment parts per linear inside one launch) and fixed
+    thresholds, on ragged row counts sharing n."""
+    n = 5120
+    ms = [1024, 2056, 520]
+    Ws = [wl.random_matrix(150 + i, m, n, "bf16") for i, m in enumerate(ms)]
+    cs = [oracle.column_norms(W) for W in Ws]
+    for mode, gs in (("stat", [dict(s_keep=s) for s in (0.1, 0.3, 0.05)]),
+                     ("fixed", [dict(tau=t) for t in (0.02, 0.05, 0.0)])):
+        layers = [_layer(fas, W, c, mode, **g) for W, c, g in zip(Ws, cs, gs)]
+        for t, kind in enumerate(["laplace", "normal", "laplace"]):
+            x = wl.random_tokens(160 + t, 1, n, "bf16", kind)[0]
+            print(f"[group {mode}] token {t}", flush=True)
+            _check_group(fas, layers, Ws, cs, gs, mode, x, f"{mode} token {t}")
+        for l in layers:
+            l.close()
+
+
+def test_group_fallbacks_and_single(fas):
+    """bf16 outputs, a deterministic handle or mixed gate modes run the
+    linears one after another; a group of one is a plain forward."""
+    n = 2048
+    Ws = [wl.random_matrix(170 + i, m, n, "bf16") for i, m in enumerate((512, 1032))]
+    cs = [oracle.column_norms(W) for W in Ws]
+    x = wl.random_tokens(171, 1, n, "bf16", "laplace")[0]
+    xd = to_dev(x, torch)
+    layers = [_layer(fas, Ws[0], cs[0], "topk", K=700), _layer(fas, Ws[1], cs[1], "stat", s_keep=0.2)]
+    refs = [oracle.forward(Ws[0], cs[0], x, "topk", K=700)["y"],
+            oracle.forward(Ws[1], cs[1], x, "stat", s_keep=0.2)["y"]]
+    for y_dtype in (torch.float32, torch.bfloat16):
+        ys = fas.SparseLinear.forward_group(layers, xd, y_dtype=y_dtype)
+        torch.cuda.synchronize()
+        for y, ref in zip(ys, refs):
+            assert rel_l2(y.float().cpu().numpy(), ref) <= REL_L2_TOL
+    layers[0].set_deterministic(True)
+    ys = fas.SparseLinear.forward_group(layers[:1], xd)
+    torch.cuda.synchronize()
+    assert rel_l2(ys[0].cpu().numpy(), refs[0]) <= REL_L2_TOL
+    for l in layers:
+        l.close()
+
+
+def test_group_graph_replays(fas):
+    """Grouped launches captured in a graph re-arm every linear's hand-off
+    and advance its generation on the device: replays match eager runs."""
+    n = 4096
+    Ws = [wl.random_matrix(180 + i, m, n, "bf16") for i, m in enumerate((2048, 1024))]
+    cs = [oracle.column_norms(W) for W in Ws]
+    layers = [_layer(fas, Ws[0], cs[0], "topk", K=1500), _layer(fas, Ws[1], cs[1], "stat", s_keep=0.15)]
+    for l in layers:
+        l.set_deterministic(False)
+    xs = [to_dev(wl.random_tokens(181 + t, 1, n, "bf16", "laplace")[0], torch) for t in range(4)]
+    # same gate mode inside a group: one group per mode, two linears each
+    pairs = [[layers[0], _layer(fas, Ws[1], cs[1], "topk", K=900)],
+             [layers[1], _layer(fas, Ws[0], cs[0], "stat", s_keep=0.25)]]
+    eager = [[y.clone() for y in fas.SparseLinear.forward_group(pairs[i % 2], x)] for i, x in enumerate(xs)]
+    torch.cuda.synchronize()
+    outs = [[torch.empty_like(y) for y in e] for e in eager]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i, x in enumerate(xs):
+            fas.SparseLinear.forward_group(pairs[i % 2], x, ys=outs[i])
+    for rep in range(3):
+        for o in outs:
+            for y in o:
+                y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for pair in pairs:
+            for l in pair:
+                l.sync_status()
+        for i in range(len(xs)):
+            for y, e in zip(outs[i], eager[i]):
+                assert rel_l2(y.cpu().numpy(), e.cpu().numpy()) <= 1e-5, f"replay {rep} group {i}"
+    for pair in pairs:
+        for l in pair:
+            l.close()
