@@ -55,7 +55,7 @@ def parse():
                     help="short eager run for memory-counter passes: 12 + 48 headline forwards "
                          "(K=5504), then three plain 256 MiB device copies; prints one line")
     ap.add_argument("--workload", default="llama7b_down",
-                    choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16"],
+                    choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16", "llama2_ffn_chain"],
                     help="llama7b_down is the headline; the others measure the remaining layer shapes")
     return ap.parse_args()
 
@@ -101,6 +101,9 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    if args.workload == "llama2_ffn_chain":
+        run_ffn_chain(args)
+        return
     if args.workload != "llama7b_down":
         run_workload(args)
         return
@@ -506,6 +509,61 @@ def run_workload(args):
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
+
+
+def run_ffn_chain(args):
+    """Sparse FFN chain of one token on Llama-2-7B FFN shapes (gate/up
+    11008 x 4096, down 4096 x 11008, bf16 std 0.02, seeded synthetic weights;
+    hidden state x ~ N(0,1)), WINA top-K at 50 % on each projection: the
+    grouped gate/up launch, the SiLU(g) u epilogue and the down projection's
+    fused forward, all on the device (sparse_linear_forward_ffn)."""
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    n, m = 4096, 11008
+    Ks = (2048, 2048, 5504)
+    shapes = ((m, n), (m, n), (n, m))
+    host = [wl.random_matrix(300 + i, a, b, "bf16") for i, (a, b) in enumerate(shapes)]
+    R = max(2, -(-(1 << 30) // sum(a * b * 2 for a, b in shapes)))
+    rings = []
+    for W, K in zip(host, Ks):
+        Wd = torch.from_numpy(np.ascontiguousarray(W).view(np.int16)).to(dev).view(torch.bfloat16)
+        rings.append([fas.SparseLinear(Wd, c=None, gate="topk", K=K) for _ in range(R)])
+        del Wd
+    NT = 64
+    X = torch.from_numpy(wl.random_tokens(310, NT, n, "bf16", "normal").view(np.int16)).to(dev).view(torch.bfloat16)
+    Y = torch.empty((R, n), dtype=torch.float32, device=dev)
+    nb = fas.sparse_linear_ffn_workspace_bytes(rings[1][0].handle)
+    WS = torch.empty((R, (nb + 255) // 256 * 256), dtype=torch.uint8, device=dev)
+
+    def step(i, s):
+        r = i % R
+        fas.sparse_linear_forward_ffn(rings[0][r].handle, rings[1][r].handle, rings[2][r].handle,
+                                      X[i % NT].data_ptr(), Y[r].data_ptr(), fas.SL_F32, WS[r].data_ptr(),
+                                      WS.shape[1], s.cuda_stream)
+    secs = _replay_timed(torch, step, args.steps, args.warmup)
+    for ring in rings:
+        for h in ring:
+            h.sync_status()
+    kept_bytes = sum(K * a * 2 for K, (a, b) in zip(Ks, shapes))
+    dense_bytes = sum(a * b * 2 for a, b in shapes)
+    us = secs / args.steps * 1e6
+    out = {"metric": "sparse FFN chain tokens/s (Llama-2-7B FFN shapes, top-K 50 % per projection)",
+           "value": args.steps / secs, "unit": "tokens/s", "ms_per_step": us * 1e-3,
+           "config": {"workload": "llama2_7b_ffn_chain_gate_up_11008x4096_down_4096x11008_bf16_topk_50pct",
+                      "K": Ks, "weight_ring_copies": R},
+           "kept_weight_bytes": kept_bytes, "dense_weight_bytes": dense_bytes,
+           "kept_GBps": kept_bytes / (us * 1e-6) / 1e9, "launches_per_token": 3,
+           "data": "synthetic", "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(out))
+    for ring in rings:
+        for h in ring:
+            h.close()
 
 
 def _replay_timed(torch, f, steps, warmup, G=60):

@@ -30,7 +30,7 @@ EXPORTED = [
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
-    "sparse_linear_forward_group",
+    "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -62,6 +62,10 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_forward_dense.restype = ctypes.c_int
     L.sparse_linear_forward_group.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _vp]
     L.sparse_linear_forward_group.restype = ctypes.c_int
+    L.sparse_linear_ffn_workspace_bytes.argtypes = [_vp]
+    L.sparse_linear_ffn_workspace_bytes.restype = _i64
+    L.sparse_linear_forward_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _vp]
+    L.sparse_linear_forward_ffn.restype = ctypes.c_int
     L.sparse_linear_get_norms.argtypes = [_vp, _vp, _vp]
     L.sparse_linear_get_norms.restype = ctypes.c_int
     L.sparse_linear_destroy.argtypes = [_vp]
@@ -117,6 +121,16 @@ def sparse_linear_forward_group(handles, x_ptr: int, y_ptrs, y_dtype: int, strea
     ya = (_vp * max(1, count))(*y_ptrs)
     _check(lib().sparse_linear_forward_group(ha, count, x_ptr, ya, y_dtype, stream or None),
            "sparse_linear_forward_group")
+
+
+def sparse_linear_ffn_workspace_bytes(up: int) -> int:
+    return int(lib().sparse_linear_ffn_workspace_bytes(up))
+
+
+def sparse_linear_forward_ffn(gate: int, up: int, down: int, x_ptr: int, y_ptr: int, y_dtype: int, ws_ptr: int,
+                              ws_bytes: int, stream: int = 0) -> None:
+    _check(lib().sparse_linear_forward_ffn(gate, up, down, x_ptr, y_ptr, y_dtype, ws_ptr, ws_bytes, stream or None),
+           "sparse_linear_forward_ffn")
 
 
 def sparse_linear_forward_dense(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, stream: int = 0) -> None:
@@ -245,6 +259,23 @@ class SparseLinear:
         sparse_linear_forward_group([l.handle for l in layers], x.data_ptr(), [y.data_ptr() for y in ys],
                                     SL_BF16 if ys[0].dtype == torch.bfloat16 else SL_F32, layers[0]._stream())
         return ys
+
+    @staticmethod
+    def forward_ffn(gate, up, down, x, y=None, y_dtype=None, workspace=None):
+        """y = down(bf16(SiLU(gate(x)) * up(x))) for one token, every step on
+        the device. Returns (y, workspace); the workspace holds g, u (fp32)
+        and h (bf16) at byte offsets 0, P and 2P, P = 256-aligned 4 * m."""
+        torch = up._torch
+        nb = sparse_linear_ffn_workspace_bytes(up.handle)
+        if workspace is None:
+            workspace = torch.empty((nb,), dtype=torch.uint8, device=up.device)
+        y_dtype = torch.float32 if y_dtype is None else y_dtype
+        if y is None:
+            y = torch.empty((down.m,), dtype=y_dtype, device=down.device)
+        sparse_linear_forward_ffn(gate.handle, up.handle, down.handle, x.data_ptr(), y.data_ptr(),
+                                  SL_BF16 if y.dtype == torch.bfloat16 else SL_F32, workspace.data_ptr(),
+                                  workspace.numel(), up._stream())
+        return y, workspace
 
     def forward_dense(self, x, y=None, y_dtype=None):
         torch = self._torch

@@ -446,6 +446,45 @@ sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, c
   }
 }
 
+// FFN workspace: g and u (fp32 [m]) and h (bf16 [m]), each 256-byte aligned.
+static int64_t ffn_piece(int64_t bytes) { return (bytes + 255) / 256 * 256; }
+static int64_t ffn_bytes(int64_t m) { return 2 * ffn_piece(4 * m) + ffn_piece(2 * m); }
+
+int64_t sparse_linear_ffn_workspace_bytes(sl_handle up) {
+  if (up == nullptr) return 0;
+  return ffn_bytes(up->m);
+}
+
+sl_status sparse_linear_forward_ffn(sl_handle gate, sl_handle up, sl_handle down, const void* x, void* y,
+                                    sl_dtype y_dtype, void* workspace, int64_t workspace_bytes, void* stream) {
+  try {
+    g_last_error.clear();
+    if (gate == nullptr || up == nullptr || down == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+    if (x == nullptr || y == nullptr || workspace == nullptr) return fail(SL_ERR_ARG, "NULL pointer");
+    if (gate->m != up->m || gate->n != up->n || down->n != up->m)
+      return fail(SL_ERR_ARG, "shapes: gate %lldx%lld, up %lldx%lld, down %lldx%lld do not chain", (long long)gate->m,
+                  (long long)gate->n, (long long)up->m, (long long)up->n, (long long)down->m, (long long)down->n);
+    if (gate->wdt != SL_BF16 || up->wdt != SL_BF16 || down->wdt != SL_BF16)
+      return fail(SL_ERR_UNSUPPORTED, "the FFN chain takes bf16 weights");
+    if (((uintptr_t)workspace % 256) != 0) return fail(SL_ERR_ARG, "workspace must be 256-byte aligned");
+    if (workspace_bytes < ffn_bytes(up->m))
+      return fail(SL_ERR_ARG, "workspace of %lld bytes, %lld needed", (long long)workspace_bytes,
+                  (long long)ffn_bytes(up->m));
+    char* ws = (char*)workspace;
+    float* g = (float*)ws;
+    float* u = (float*)(ws + ffn_piece(4 * up->m));
+    uint16_t* hb = (uint16_t*)(ws + 2 * ffn_piece(4 * up->m));
+    const sl_handle gu[2] = {gate, up};
+    void* const ys[2] = {g, u};
+    sl_status st = sparse_linear_forward_group(gu, 2, x, ys, SL_F32, stream);
+    if (st != SL_OK) return st;
+    SL_HIP(sl::launch_silu_mul(g, u, hb, up->m, (hipStream_t)stream));
+    return forward_impl(down, hb, 1, y, y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_ffn");
+  }
+}
+
 sl_status sparse_linear_forward_dense(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                       void* stream) {
   try {

@@ -125,6 +125,8 @@ hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_o
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
                           void* y, sl_dtype ydt, hipStream_t s);
+// h = bf16(SiLU(g) * u) over m values (sparse FFN chain epilogue).
+hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t m, hipStream_t s);
 // Grouped fused forward (one token) of count <= 8 linears that share x: all
 // fused_supported, the same n and gate mode, fp32 y, atomic reduction.
 constexpr int kMaxGroupLinears = 8;

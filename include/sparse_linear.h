@@ -150,6 +150,32 @@ sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, c
                                       sl_dtype y_dtype, void* stream);
 
 /*
+ * Sparse FFN chain for one token (Spark Transformer article, section 2.1: the
+ * FFN scores, selects and computes only the selected part; WINA article,
+ * section 一: each projection keeps its inputs by |x_j c_j|):
+ *
+ *   g = gate(x), u = up(x)     one grouped launch (sparse_linear_forward_group)
+ *   h = bf16(SiLU(g) * u)      SiLU(v) = v / (1 + exp(-v)) in fp32, then one
+ *                              round to nearest even
+ *   y = down(h)                the down projection's own gate on h
+ *
+ *   gate, up   handles with the same shape [m][n] (bf16 weights).
+ *   down       handle of shape [m2][m] (bf16 weights): its input is h.
+ *   x          device [n] bf16.
+ *   y          device [m2] of y_dtype.
+ *   workspace  device memory the caller owns, 256-byte aligned, of at least
+ *              sparse_linear_ffn_workspace_bytes(up) bytes: g and u (fp32 [m])
+ *              and h (bf16 [m]) are left there after the call.
+ *
+ * Errors: NULL arguments, shapes that do not chain, a short or misaligned
+ * workspace (SL_ERR_ARG); weights other than bf16 (SL_ERR_UNSUPPORTED).
+ * Asynchronous on `stream`; the workspace is in use until it completes.
+ */
+int64_t sparse_linear_ffn_workspace_bytes(sl_handle up);
+sl_status sparse_linear_forward_ffn(sl_handle gate, sl_handle up, sl_handle down, const void* x, void* y,
+                                    sl_dtype y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
+
+/*
  * sparse_linear_forward_dense -- y = W x for B tokens with every input kept,
  * run by the same product kernel as the sparse path over the identity index
  * list (the dense baseline the sparse forward is compared against).

@@ -106,6 +106,13 @@ def test_forward_rejects_null_handle_and_pointers(slib):
     assert L.sparse_linear_sync_status(None, None) == 1
 
 
+def test_forward_ffn_rejects_bad_arguments(slib):
+    L = slib.lib()
+    assert L.sparse_linear_ffn_workspace_bytes(None) == 0
+    assert L.sparse_linear_forward_ffn(None, None, None, 1, 1, 0, 1, 1 << 20, None) == 1
+    assert "NULL" in slib.sparse_linear_last_error()
+
+
 def test_forward_group_rejects_bad_arguments(slib):
     L = slib.lib()
     hs = (ctypes.c_void_p * 2)(None, None)
