@@ -17,7 +17,12 @@ Every function restates, in plain slow code, what the pages define:
   index-list product): y accumulates x_j times the weight vector of input j
   over the active indices only.
 
-Parity status of each function is listed in ``oracle.sparse_linear``.
+* Double Sparsity article, section 在线前向计算 (online forward): decode
+  attention over the tokens whose label-channel scores are the k largest
+  (``oracle.double_sparse``).
+
+Parity status of each function is listed in ``oracle.sparse_linear`` and
+``oracle.double_sparse``.
 """
 from .sparse_linear import (  # noqa: F401
     as_f64,
@@ -34,3 +39,4 @@ from .sparse_linear import (  # noqa: F401
     gate,
     forward,
 )
+from . import double_sparse  # noqa: F401,E402
