@@ -1,12 +1,14 @@
 """Python binding of the weight-informed activation-sparse linear (C ABI in
-include/sparse_linear.h, HIP kernels for gfx950 in csrc/).
+include/sparse_linear.h) and of Double Sparsity decode attention (C ABI in
+include/double_sparse.h); HIP kernels for gfx950 in csrc/.
 
 Argument marshalling only: every step of the forward runs in the library's
 kernels. PyTorch supplies device memory and streams. Loading fails loudly when
 the built library is missing; there is no fallback path.
 
 The functions below carry the C names; ``SparseLinear`` wraps a handle for
-torch tensors.
+torch tensors; ``label_cache_update`` and ``decode_attention`` take torch
+tensors for the Double Sparsity calls.
 """
 from __future__ import annotations
 
@@ -23,6 +25,7 @@ SL_W_ROWMAJOR_OUT_IN, SL_W_COLMAJOR = 0, 1
 SL_GATE_TOPK, SL_GATE_STAT, SL_GATE_FIXED = 0, 1, 2
 SL_MAX_N, SL_MAX_BATCH = 32768, 16
 SL_STAGE_GATE, SL_STAGE_PRODUCT = 1, 2
+DS_MAX_SEQ, DS_MAX_K = 32768, 8192
 
 EXPORTED = [
     "sparse_linear_init", "sparse_linear_forward", "sparse_linear_forward_dense",
@@ -31,6 +34,7 @@ EXPORTED = [
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
     "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
+    "ds_label_cache_update", "ds_decode_attention",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -88,6 +92,11 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_set_fused.restype = ctypes.c_int
     L.sparse_linear_sync_status.argtypes = [_vp, _vp]
     L.sparse_linear_sync_status.restype = ctypes.c_int
+    L.ds_label_cache_update.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
+    L.ds_label_cache_update.restype = ctypes.c_int
+    L.ds_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                      ctypes.c_float, _vp, _vp, _vp]
+    L.ds_decode_attention.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -131,6 +140,20 @@ def sparse_linear_forward_ffn(gate: int, up: int, down: int, x_ptr: int, y_ptr: 
                               ws_bytes: int, stream: int = 0) -> None:
     _check(lib().sparse_linear_forward_ffn(gate, up, down, x_ptr, y_ptr, y_dtype, ws_ptr, ws_bytes, stream or None),
            "sparse_linear_forward_ffn")
+
+
+def ds_label_cache_update(key_ptr: int, label_ptr: int, channels_ptr: int, start_ptr: int, batch: int, heads: int,
+                          max_seq: int, head_dim: int, r: int, span: int, stream: int = 0) -> None:
+    _check(lib().ds_label_cache_update(key_ptr, label_ptr, channels_ptr, start_ptr or None, batch, heads, max_seq,
+                                       head_dim, r, span, stream or None), "ds_label_cache_update")
+
+
+def ds_decode_attention(q_ptr: int, key_ptr: int, value_ptr: int, label_ptr: int, channels_ptr: int,
+                        seq_len_ptr: int, batch: int, heads: int, max_seq: int, head_dim: int, r: int, k: int,
+                        scale: float, out_ptr: int, tokens_out_ptr: int = 0, stream: int = 0) -> None:
+    _check(lib().ds_decode_attention(q_ptr, key_ptr, value_ptr, label_ptr or None, channels_ptr, seq_len_ptr,
+                                     batch, heads, max_seq, head_dim, r, k, scale, out_ptr,
+                                     tokens_out_ptr or None, stream or None), "ds_decode_attention")
 
 
 def sparse_linear_forward_dense(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype: int, stream: int = 0) -> None:
@@ -317,3 +340,40 @@ class SparseLinear:
             self.close()
         except Exception:
             pass
+
+
+# --------------------------------------------- Double Sparsity decode attention
+def _stream_of(t):
+    import torch
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def label_cache_update(key, label, channels, start=None, span=None) -> None:
+    """Copy the label channels of key [B][H][S][d] (bf16) into label
+    [B][H][S][r] for tokens start[b] .. start[b] + span - 1 (start: int32
+    [B] on the device, or None for 0; span: default S)."""
+    B, H, S, d = key.shape
+    r = channels.shape[1]
+    ds_label_cache_update(key.data_ptr(), label.data_ptr(), channels.data_ptr(),
+                          0 if start is None else start.data_ptr(), B, H, S, d, r,
+                          S if span is None else int(span), _stream_of(key))
+
+
+def decode_attention(q, key, value, label, channels, seq_len, k: int, scale: Optional[float] = None,
+                     out=None, tokens_out: bool = False):
+    """One Double Sparsity decode step: q [B][H][d], key/value [B][H][S][d],
+    label [B][H][S][r] (bf16), channels [H][r] and seq_len [B] (int32), all
+    on one device. Returns out [B][H][d] fp32, or (out, tokens [B][H][k]
+    int32) with tokens_out."""
+    import torch
+    B, H, S, d = key.shape
+    r = channels.shape[1]
+    if scale is None:
+        scale = d ** -0.5
+    if out is None:
+        out = torch.empty((B, H, d), dtype=torch.float32, device=q.device)
+    toks = torch.empty((B, H, k), dtype=torch.int32, device=q.device) if tokens_out else None
+    ds_decode_attention(q.data_ptr(), key.data_ptr(), value.data_ptr(), 0 if label is None else label.data_ptr(),
+                        channels.data_ptr(), seq_len.data_ptr(), B, H, S, d, r, k, float(scale), out.data_ptr(),
+                        0 if toks is None else toks.data_ptr(), _stream_of(q))
+    return (out, toks) if tokens_out else out

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_linear.so")
-SOURCES = ["api.cpp", "layout.hip", "gate.hip", "product.hip", "fused.hip", "union_product.hip", "ffn.hip"]
+SOURCES = ["api.cpp", "layout.hip", "gate.hip", "product.hip", "fused.hip", "union_product.hip", "ffn.hip", "double_sparse.hip"]
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
@@ -62,7 +62,7 @@ def is_stale() -> bool:
         return True
     t = os.path.getmtime(LIB)
     deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)]
-    deps.append(os.path.join(os.path.dirname(HERE), "include", "sparse_linear.h"))
+    deps += [os.path.join(os.path.dirname(HERE), "include", f) for f in ("sparse_linear.h", "double_sparse.h")]
     return any(os.path.getmtime(d) > t for d in deps if os.path.exists(d))
 
 

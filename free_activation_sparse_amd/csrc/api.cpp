@@ -569,3 +569,101 @@ sl_status sparse_linear_set_plan(sl_handle h, int32_t rows_per_tile, int32_t spl
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------ Double Sparsity
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+sl_status ds_check_shape(int32_t batch, int32_t heads, int32_t max_seq, int32_t head_dim, int32_t r) {
+  if (batch < 1 || heads < 1) return fail(SL_ERR_ARG, "batch=%d and heads=%d must be >= 1", (int)batch, (int)heads);
+  if ((int64_t)batch * heads > INT32_MAX) return fail(SL_ERR_ARG, "batch * heads exceeds 2^31 - 1");
+  if (max_seq < 1 || max_seq > DS_MAX_SEQ)
+    return fail(SL_ERR_ARG, "max_seq=%d outside [1, %d]", (int)max_seq, DS_MAX_SEQ);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(SL_ERR_UNSUPPORTED, "head_dim=%d: 64 and 128 are supported", (int)head_dim);
+  if (r != 8 && r != 16 && r != 32) return fail(SL_ERR_UNSUPPORTED, "r=%d: 8, 16 and 32 are supported", (int)r);
+  return SL_OK;
+}
+
+sl_status ds_device() {
+  int dev = 0;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  return SL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sl_status ds_label_cache_update(const void* key, void* label, const int32_t* channels, const int32_t* start,
+                                int32_t batch, int32_t heads, int32_t max_seq, int32_t head_dim, int32_t r,
+                                int32_t span, void* stream) {
+  try {
+    g_last_error.clear();
+    if (key == nullptr || label == nullptr || channels == nullptr)
+      return fail(SL_ERR_ARG, "key, label and channels must not be NULL");
+    const sl_status st = ds_check_shape(batch, heads, max_seq, head_dim, r);
+    if (st != SL_OK) return st;
+    if (span < 0) return fail(SL_ERR_ARG, "span=%d must be >= 0", (int)span);
+    if (!aligned(label, 16)) return fail(SL_ERR_UNSUPPORTED, "label must be 16-byte aligned");
+    if (!aligned(key, 2) || !aligned(channels, 4) || (start != nullptr && !aligned(start, 4)))
+      return fail(SL_ERR_ARG, "key, channels or start misaligned for its element type");
+    if (span == 0) return SL_OK;
+    const sl_status sd = ds_device();
+    if (sd != SL_OK) return sd;
+    SL_HIP(sl::launch_ds_label((const uint16_t*)key, (uint16_t*)label, channels, start, batch, heads, max_seq,
+                               head_dim, r, std::min<int32_t>(span, DS_MAX_SEQ), (hipStream_t)stream));
+    return SL_OK;
+  } catch (...) {
+    return fail(SL_ERR_HIP, "unexpected exception");
+  }
+}
+
+sl_status ds_decode_attention(const void* q, const void* key, const void* value, const void* label,
+                              const int32_t* channels, const int32_t* seq_len, int32_t batch, int32_t heads,
+                              int32_t max_seq, int32_t head_dim, int32_t r, int32_t k, float scale, float* out,
+                              int32_t* tokens_out, void* stream) {
+  try {
+    g_last_error.clear();
+    if (q == nullptr || key == nullptr || value == nullptr || channels == nullptr || seq_len == nullptr ||
+        out == nullptr)
+      return fail(SL_ERR_ARG, "q, key, value, channels, seq_len and out must not be NULL");
+    const sl_status st = ds_check_shape(batch, heads, max_seq, head_dim, r);
+    if (st != SL_OK) return st;
+    if (k < 1) return fail(SL_ERR_ARG, "k=%d must be >= 1", (int)k);
+    if (k < max_seq && k > DS_MAX_K)
+      return fail(SL_ERR_UNSUPPORTED, "k=%d: at most %d kept tokens unless k >= max_seq", (int)k, DS_MAX_K);
+    if (k < max_seq && label == nullptr) return fail(SL_ERR_ARG, "label must not be NULL when k < max_seq");
+    if (!std::isfinite(scale)) return fail(SL_ERR_ARG, "scale must be finite");
+    const size_t row_align = head_dim == 128 ? 16 : 8;
+    if (!aligned(q, row_align) || !aligned(key, row_align) || !aligned(value, row_align))
+      return fail(SL_ERR_UNSUPPORTED, "q, key and value must be %d-byte aligned", (int)row_align);
+    if (label != nullptr && !aligned(label, 16)) return fail(SL_ERR_UNSUPPORTED, "label must be 16-byte aligned");
+    if (!aligned(out, 4) || !aligned(channels, 4) || !aligned(seq_len, 4) ||
+        (tokens_out != nullptr && !aligned(tokens_out, 4)))
+      return fail(SL_ERR_ARG, "out, channels, seq_len or tokens_out misaligned for its element type");
+    const sl_status sd = ds_device();
+    if (sd != SL_OK) return sd;
+    sl::DsDecodeParams p;
+    p.q = (const uint16_t*)q;
+    p.key = (const uint16_t*)key;
+    p.value = (const uint16_t*)value;
+    p.label = (const uint16_t*)label;
+    p.channels = channels;
+    p.seq_len = seq_len;
+    p.heads = heads;
+    p.max_seq = max_seq;
+    p.k = k;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.out = out;
+    p.tokens_out = tokens_out;
+    SL_HIP(sl::launch_ds_decode(p, batch, head_dim, r, (hipStream_t)stream));
+    return SL_OK;
+  } catch (...) {
+    return fail(SL_ERR_HIP, "unexpected exception");
+  }
+}
+
+}  // extern "C"

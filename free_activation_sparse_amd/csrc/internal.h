@@ -7,6 +7,7 @@
 
 #include <vector>
 
+#include "double_sparse.h"
 #include "sparse_linear.h"
 
 namespace sl {
@@ -137,6 +138,22 @@ hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void*
 bool fused_supported(const sl_linear* h, const void* x);
 hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
                         double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s);
+// Double Sparsity decode attention (layouts and semantics in double_sparse.h).
+struct DsDecodeParams {
+  const uint16_t* q;
+  const uint16_t* key;
+  const uint16_t* value;
+  const uint16_t* label;
+  const int32_t* channels;
+  const int32_t* seq_len;
+  int heads, max_seq, k;
+  float scale_log2;  // softmax scale * log2(e)
+  float* out;
+  int32_t* tokens_out;
+};
+hipError_t launch_ds_decode(const DsDecodeParams& p, int batch, int head_dim, int r, hipStream_t s);
+hipError_t launch_ds_label(const uint16_t* key, uint16_t* label, const int32_t* channels, const int32_t* start,
+                           int batch, int heads, int max_seq, int head_dim, int r, int span, hipStream_t s);
 // Union-product workgroups resident per compute unit (occupancy query).
 int union_workgroups_per_cu(int rows, sl_dtype ydt, bool atomic);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,

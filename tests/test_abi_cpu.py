@@ -10,12 +10,15 @@ import statistics
 import numpy as np
 import pytest
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sparse_linear.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+HEADERS = [os.path.join(INCLUDE, "sparse_linear.h"), os.path.join(INCLUDE, "double_sparse.h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(sparse_linear_\w+)\s*\(", text)))
+    names = set()
+    for hp in HEADERS:
+        names |= set(re.findall(r"\b((?:sparse_linear|ds)_\w+)\s*\(", open(hp).read()))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(slib):
@@ -131,3 +134,40 @@ def test_strerror(slib):
     assert slib.sparse_linear_strerror(0) == "success"
     assert slib.sparse_linear_strerror(2) == "unsupported shape or alignment"
     assert slib.sparse_linear_strerror(99) == "unknown status"
+
+
+# ------------------------------------------------ Double Sparsity entry points
+_P = 1 << 20  # a 1 MiB-aligned stand-in address: checks reject before any device access
+
+
+def _ds(slib, q=_P, key=_P, value=_P, label=_P, ch=_P, sl=_P, B=2, H=4, S=128, d=128, r=16, k=8, scale=0.1,
+        out=_P, toks=0):
+    return slib.lib().ds_decode_attention(q or None, key or None, value or None, label or None, ch or None,
+                                          sl or None, B, H, S, d, r, k, scale, out or None, toks or None, None)
+
+
+@pytest.mark.parametrize("kw, status", [
+    (dict(q=0), 1), (dict(key=0), 1), (dict(value=0), 1), (dict(ch=0), 1), (dict(sl=0), 1), (dict(out=0), 1),
+    (dict(label=0), 1),                       # label needed while k < max_seq
+    (dict(B=0), 1), (dict(H=0), 1), (dict(S=0), 1), (dict(S=32769), 1),
+    (dict(d=96), 2), (dict(d=256), 2), (dict(r=12), 2), (dict(r=64), 2),
+    (dict(k=0), 1), (dict(k=-3), 1), (dict(S=20000, k=8193), 2),
+    (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
+    (dict(label=_P + 8), 2), (dict(q=_P + 8), 2), (dict(d=64, q=_P + 4), 2), (dict(out=_P + 2), 1),
+    (dict(toks=_P + 2), 1), (dict(B=1 << 16, H=1 << 16), 1),
+])
+def test_ds_decode_rejects(slib, kw, status):
+    assert _ds(slib, **kw) == status
+    assert slib.lib().sparse_linear_last_error()
+
+
+def test_ds_label_update_rejects(slib):
+    L = slib.lib()
+    f = lambda **kw: L.ds_label_cache_update(kw.get("key", _P) or None, kw.get("label", _P) or None,
+                                             kw.get("ch", _P) or None, kw.get("start", 0) or None,
+                                             kw.get("B", 2), kw.get("H", 4), kw.get("S", 128), kw.get("d", 128),
+                                             kw.get("r", 16), kw.get("span", 128), None)
+    assert f(key=0) == 1 and f(label=0) == 1 and f(ch=0) == 1
+    assert f(d=32) == 2 and f(r=4) == 2 and f(S=0) == 1 and f(span=-1) == 1
+    assert f(label=_P + 4) == 2 and f(start=_P + 2) == 1
+    assert f(span=0) == 0          # nothing to do: no device access
