@@ -55,7 +55,8 @@ def parse():
                     help="short eager run for memory-counter passes: 12 + 48 headline forwards "
                          "(K=5504), then three plain 256 MiB device copies; prints one line")
     ap.add_argument("--workload", default="llama7b_down",
-                    choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16", "llama2_ffn_chain"],
+                    choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16", "llama2_ffn_chain",
+                             "llama2_ds_decode"],
                     help="llama7b_down is the headline; the others measure the remaining layer shapes")
     return ap.parse_args()
 
@@ -103,6 +104,9 @@ def main():
 
     if args.workload == "llama2_ffn_chain":
         run_ffn_chain(args)
+        return
+    if args.workload == "llama2_ds_decode":
+        run_ds_decode(args)
         return
     if args.workload != "llama7b_down":
         run_workload(args)
@@ -564,6 +568,101 @@ def run_ffn_chain(args):
     for ring in rings:
         for h in ring:
             h.close()
+
+
+def ds_algorithmic_bytes(B, H, n, d, r, k):
+    """Bytes one Double Sparsity decode launch must move when every sequence
+    holds n tokens: label rows of all n tokens (r bf16 each), the key and value
+    rows of the min(k, n) kept tokens (d bf16 each), q (d bf16), the channel
+    list (r int32), out (d fp32), and the lengths (int32). A dense step
+    (k >= n) reads no label rows."""
+    kept = min(k, n)
+    label = n * r * 2 if k < n else 0
+    return B * H * (label + kept * d * 2 * 2 + d * 2 + d * 4) + H * r * 4 + B * 4
+
+
+def run_ds_decode(args):
+    """Double Sparsity decode attention for one Llama-2-7B attention layer:
+    16 sequences of 8192 cached tokens, 32 heads of 128 channels, bf16 caches
+    with 8 seeded outlier channels per head (synthetic; see
+    workloads/decode_attention.py). Legs: 1/16 of the channels and 1/16 of the
+    tokens (r = 8, k = 512, the pages' headline sparsity), the SGLang example's
+    r = 16, k = 256, and the same kernel attending to every token (dense).
+    Caches rotate through copies so that a step never finds the previous
+    step's rows in the 256 MB Infinity Cache; steps are replayed from HIP
+    graphs."""
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    from workloads import decode_attention as wda
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = wda.CASES["llama2_7b_b16_s8192_r8_k512"]
+    inp = wda.make_inputs(base)
+    B, H, S, d = inp.key.shape
+    order = wda.channel_order(base)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    R = 3
+    Q = bf(inp.q)
+    Ks, Vs = [bf(inp.key)], [bf(inp.value)]
+    for _ in range(R - 1):
+        Ks.append(Ks[0].clone())
+        Vs.append(Vs[0].clone())
+    del inp
+    sl = torch.full((B,), S, dtype=torch.int32, device=dev)
+    last = sl - 1
+    out = torch.empty((R, B, H, d), dtype=torch.float32, device=dev)
+    legs = {}
+    for name, r, k in (("r8_k512", 8, 512), ("r16_k256", 16, 256), ("dense", 8, S)):
+        ch = torch.from_numpy(np.ascontiguousarray(order[:, :r])).to(dev)
+        Ls = []
+        if k < S:
+            for i in range(R):
+                L = torch.empty((B, H, S, r), dtype=torch.bfloat16, device=dev)
+                fas.label_cache_update(Ks[i], L, ch)
+                Ls.append(L)
+        scale = d ** -0.5
+
+        def step(i, s, r=r, k=k, ch=ch, Ls=Ls):
+            j = i % R
+            fas.ds_decode_attention(Q.data_ptr(), Ks[j].data_ptr(), Vs[j].data_ptr(),
+                                    Ls[j].data_ptr() if Ls else 0, ch.data_ptr(), sl.data_ptr(), B, H, S, d, r, k,
+                                    scale, out[j].data_ptr(), 0, s.cuda_stream)
+        steps = args.steps if k < S else max(20, args.steps // 10)
+        secs = _replay_timed(torch, step, steps, min(args.warmup, steps))
+        kus = _graph_us(torch, step, count=120 if k < S else 30)
+        nbytes = ds_algorithmic_bytes(B, H, S, d, r, k)
+        legs[name] = {"r": r, "k": k, "us_per_step": secs / steps * 1e6, "kernel_us": kus,
+                      "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (kus * 1e-6) / 1e9,
+                      "sequences_per_s": B * steps / secs}
+        if Ls:
+            # decode append: the newest token of every sequence (position seq_len - 1)
+            upd = lambda i, s, L=Ls[0], ch=ch, r=r: fas.ds_label_cache_update(
+                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), last.data_ptr(), B, H, S, d, r, 1, s.cuda_stream)
+            legs[name]["label_append_us"] = _graph_us(torch, upd, count=120)
+            pre = lambda i, s, L=Ls[0], ch=ch, r=r: fas.ds_label_cache_update(
+                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), 0, B, H, S, d, r, S, s.cuda_stream)
+            legs[name]["label_prefill_us"] = _graph_us(torch, pre, count=20)
+        del Ls
+    head = legs["r8_k512"]
+    for name in ("r8_k512", "r16_k256"):
+        legs[name]["speedup_vs_dense"] = legs["dense"]["kernel_us"] / legs[name]["kernel_us"]
+    res = {"metric": "Double Sparsity decode attention sequences/s (one layer) & achieved HBM GB/s",
+           "value": head["sequences_per_s"], "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": head["us_per_step"] * 1e-3, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "llama2_7b_ds_decode_b16_h32_d128_s8192_r8_k512", "batch": B, "heads": H,
+                      "head_dim": d, "seq_len": S, "label_channels": 8, "heavy_tokens": 512,
+                      "cache_ring_copies": R, "launch": "graph"},
+           "roofline": {"bound": "hbm", "achieved": round(head["achieved_GBps"], 1), "peak": PEAK_GBS,
+                        "unit": "GB/s", "frac": round(head["achieved_GBps"] / PEAK_GBS, 4), "traffic": None,
+                        "kernel": "ds_decode_kernel", "kernel_us": round(head["kernel_us"], 2),
+                        "algorithmic_bytes": head["algorithmic_bytes"]},
+           "legs": legs, "device": torch.cuda.get_device_name(0)}
+    print(json.dumps(res))
 
 
 def _replay_timed(torch, f, steps, warmup, G=60):

@@ -19,7 +19,8 @@
 //      rows per lane), 64 rows per workgroup step, four steps of key and value
 //      loads in flight; each 16-lane row keeps its own online softmax (running
 //      max, sum, fp32 accumulators, exp2 with the scale folded into log2 e);
-//      the 64 rows merge through LDS at the end.
+//      the rows merge by cross-lane shuffles within each wavefront, then the
+//      16 wavefront partials through LDS.
 // A sequence with n <= k tokens skips steps 1-3 and attends to all n.
 //
 // ds_label_kernel: one thread per (sequence, head, token): the r channels of
@@ -95,21 +96,22 @@ template <int D, int R, int E>
 __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDecodeParams a) {
   constexpr int VE = D / 16;  // key/value elements per lane
   constexpr int RV = R / 8;   // 16-byte loads per label row
-  constexpr int EB = RV >= 4 ? 2 : (RV == 2 ? 4 : 8);  // tokens per label batch (32 registers of loads)
+  constexpr int EB = RV >= 4 ? 1 : (RV == 2 ? 2 : 4);  // tokens per label batch (16 registers of loads)
   // dynamic LDS: selection histograms (32 KB), then the kept list, then the
-  // per-row attention partials (64 x D floats); each use ends before the next
+  // per-wavefront attention partials (16 x D floats); each use ends before
+  // the next
   extern __shared__ __align__(16) uint32_t dyn[];
   __shared__ uint32_t h3[256], hi1[256], hi2[128];
   __shared__ uint32_t wsum[GW];
   __shared__ uint32_t res[4];
   __shared__ uint64_t cand[64];
   __shared__ uint32_t cnt[E * GW];
-  __shared__ float rowm[kRows], rowl[kRows];
+  __shared__ float wm[GW], wl[GW];
 
   uint32_t* h1 = dyn;
   uint32_t* h2 = dyn + 4096;
   int32_t* sel = (int32_t*)dyn;
-  float* rowacc = (float*)dyn;
+  float* wacc = (float*)dyn;
 
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const int bh = blockIdx.x;
@@ -188,7 +190,7 @@ __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDec
       if (d < 4096u) atomicAdd(&h1[d], 1u);
     }
     __syncthreads();
-    if (w == 0) find_bin_wave<4096, (E <= 16 ? 8 : 2)>(h1, K, res);
+    if (w == 0) find_bin_wave<4096, 2>(h1, K, res);  // few reads in flight: registers are scarce here
     __syncthreads();
     const bool in_window = res[0] != 0xffffffffu;
     const uint32_t c1 = in_window ? res[2] : 0u;
@@ -364,23 +366,41 @@ __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDec
       m = mx;
     }
   }
-  __syncthreads();  // the kept list is dead: the row partials reuse its LDS
-  if (p == 0) {
-    rowm[row] = m;
-    rowl[row] = l;
-  }
+  // merge the four rows of each wavefront (lanes l, l + 16, l + 32, l + 48
+  // hold the same columns), then the 16 wavefronts through LDS
+  const float mw = fmaxf(fmaxf(m, __shfl_xor(m, 16)), fmaxf(__shfl_xor(m, 32), __shfl_xor(m, 48)));
+  const float sc = m == -INFINITY ? 0.f : exp2f(m - mw);  // an empty row weighs nothing
+  float lw = l * sc;
+  lw += __shfl_xor(lw, 16);
+  lw += __shfl_xor(lw, 32);
 #pragma unroll
-  for (int e = 0; e < VE; ++e) rowacc[row * D + p * VE + e] = acc[e];
+  for (int e = 0; e < VE; ++e) {
+    float v = acc[e] * sc;
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    acc[e] = v;
+  }
+  __syncthreads();  // the kept list is dead: the wavefront partials reuse its LDS
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < VE; ++e) wacc[w * D + lane * VE + e] = acc[e];
+  }
+  if (lane == 0) {
+    wm[w] = mw;
+    wl[w] = lw;
+  }
   __syncthreads();
   if (t < D) {
     float M = -INFINITY;
-    for (int r = 0; r < kRows; ++r) M = fmaxf(M, rowm[r]);
+#pragma unroll
+    for (int q = 0; q < GW; ++q) M = fmaxf(M, wm[q]);
     float L = 0.f, O = 0.f;
     if (M != -INFINITY) {
-      for (int r = 0; r < kRows; ++r) {
-        const float wr = exp2f(rowm[r] - M);
-        L = fmaf(wr, rowl[r], L);
-        O = fmaf(wr, rowacc[r * D + t], O);
+#pragma unroll
+      for (int q = 0; q < GW; ++q) {
+        const float wq = exp2f(wm[q] - M);  // 0 for a wavefront without rows
+        L = fmaf(wq, wl[q], L);
+        O = fmaf(wq, wacc[q * D + t], O);
       }
     }
     a.out[(size_t)bh * D + t] = M == -INFINITY ? 0.f : O / L;
@@ -414,7 +434,7 @@ hipError_t go_decode(const sl::DsDecodeParams& p, int batch, hipStream_t s) {
   const int kl = p.k < p.max_seq ? p.k : 0;  // kept-list entries (0: every sequence dense)
   size_t dyn = 4096 * 2 * sizeof(uint32_t);
   dyn = std::max(dyn, (size_t)kl * sizeof(int32_t));
-  dyn = std::max(dyn, (size_t)kRows * D * sizeof(float));
+  dyn = std::max(dyn, (size_t)GW * D * sizeof(float));
   ds_decode_kernel<D, R, E><<<(unsigned)(batch * p.heads), GT, dyn, s>>>(p);
   return hipGetLastError();
 }
