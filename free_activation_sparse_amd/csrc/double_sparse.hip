@@ -40,7 +40,6 @@ namespace {
 using namespace sl::dev;
 using sl::gatedev::GT;
 using sl::gatedev::GW;
-using sl::gatedev::block_incl_scan;
 using sl::gatedev::find_bin;
 using sl::gatedev::find_bin_wave;
 
@@ -96,7 +95,7 @@ template <int D, int R, int E>
 __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDecodeParams a) {
   constexpr int VE = D / 16;  // key/value elements per lane
   constexpr int RV = R / 8;   // 16-byte loads per label row
-  constexpr int EB = RV >= 4 ? 1 : (RV == 2 ? 2 : 4);  // tokens per label batch (16 registers of loads)
+  constexpr int EB = RV >= 4 ? 1 : (RV == 2 ? 2 : 8);  // tokens per label batch (16 or 32 registers of loads)
   // dynamic LDS: selection histograms (32 KB), then the kept list, then the
   // per-wavefront attention partials (16 x D floats); each use ends before
   // the next
@@ -296,14 +295,27 @@ __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDec
       if (lane == 0) cnt[e * GW + w] = c;
     }
     __syncthreads();
-    const uint32_t cv = t < E * GW ? cnt[t] : 0u;
-    const uint32_t incl = block_incl_scan(cv, wsum);
-    if (t < E * GW) cnt[t] = incl - cv;
-    __syncthreads();
+    // every wavefront scans the E * 16 counts (slot-major, so in token order)
+    // itself and reads off its own offsets: one block barrier, not three
+    constexpr int CPL = (E * GW + 63) / 64;  // counts per lane
+    uint32_t pre[CPL];
+    uint32_t lsum = 0u;
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) {
+      const int idx = lane * CPL + q;
+      pre[q] = lsum;
+      lsum += idx < E * GW ? cnt[idx] : 0u;
+    }
+    const uint32_t lexcl = wave_incl_scan(lsum) - lsum;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
+      const int idx = e * GW + w;  // wavefront-uniform
+      uint32_t mine = 0u;
+#pragma unroll
+      for (int q = 0; q < CPL; ++q) mine = (idx % CPL == q) ? pre[q] : mine;
+      const uint32_t off = (uint32_t)__builtin_amdgcn_readlane((int)(lexcl + mine), idx / CPL);
       const uint64_t bal = __ballot(kept(e));
-      if ((bal >> lane) & 1ull) sel[cnt[e * GW + w] + lanes_below(bal)] = e * GT + t;
+      if ((bal >> lane) & 1ull) sel[off + lanes_below(bal)] = e * GT + t;
     }
     __syncthreads();
   }
