@@ -52,3 +52,31 @@ def test_config3_shared_inputs():
     np.testing.assert_array_equal(q, k)
     np.testing.assert_array_equal(q, up)
     assert not np.array_equal(q, o)
+
+
+# ------------------------------------------- Double Sparsity decode inputs
+def test_decode_inputs_seeded_and_prefix_stable():
+    from workloads import decode_attention as wda
+    c = wda.DecodeCase("t", 3, 4, 64, 50, 8, 5, ragged=True, seed=7)
+    a, b = wda.make_inputs(c), wda.make_inputs(c)
+    for f in ("q", "key", "value", "channels", "seq_len"):
+        assert np.array_equal(getattr(a, f), getattr(b, f))
+    p = wda.make_inputs(c, batch=2)          # the first sequences of the full case
+    assert np.array_equal(p.key, a.key[:2]) and np.array_equal(p.q, a.q[:2])
+    assert np.all((a.seq_len >= 1) & (a.seq_len <= 50))
+    assert a.key.dtype == np.uint16 and a.channels.dtype == np.int32
+
+
+def test_decode_inputs_outlier_channels():
+    # the channel list starts with the heavy channels, whose keys are scaled up
+    from workloads import decode_attention as wda
+    c = wda.DecodeCase("t", 2, 3, 128, 4000, 16, 10, seed=8)
+    inp = wda.make_inputs(c)
+    kf = (inp.key.astype(np.uint32) << 16).view(np.float32)
+    std = kf.std(axis=(0, 2))                # per (head, channel)
+    for h in range(3):
+        heavy = inp.channels[h, :c.heavy]
+        rest = np.setdiff1d(np.arange(128), heavy)
+        assert np.all(np.abs(std[h, heavy] - c.outlier_scale) < 0.2)
+        assert np.all(np.abs(std[h, rest] - 1.0) < 0.1)
+        assert len(set(inp.channels[h].tolist())) == 16
