@@ -93,13 +93,13 @@ struct RowPart<4> {
   }
 };
 
-// Up to 8192 tokens (E = 8) two workgroups share a compute unit (at most 64
-// registers per lane); up to 32768 (E = 32) one does.
+// Up to 16384 tokens (E = 8 or 16) two workgroups share a compute unit (at
+// most 64 registers per lane); up to 32768 (E = 32) one does.
 template <int D, int R, int E>
-__global__ __launch_bounds__(GT, E <= 8 ? 8 : 4) void ds_decode_kernel(sl::DsDecodeParams a) {
+__global__ __launch_bounds__(GT, E <= 16 ? 8 : 4) void ds_decode_kernel(sl::DsDecodeParams a) {
   constexpr int VE = D / 16;  // key/value elements per lane
   constexpr int RV = R / 8;   // 16-byte loads per label row
-  constexpr int EB = RV >= 4 ? 1 : (RV == 2 ? 2 : 8);  // tokens per label batch (16 or 32 registers of loads)
+  constexpr int EB = RV >= 4 ? 1 : (RV == 2 ? (E <= 8 ? 2 : 1) : (E <= 8 ? 8 : 2));  // tokens per label batch
   // dynamic LDS: selection histograms (32 KB), then the kept list, then the
   // per-wavefront attention partials (16 x D floats); each use ends before
   // the next
@@ -458,6 +458,7 @@ hipError_t go_decode(const sl::DsDecodeParams& p, int batch, hipStream_t s) {
 template <int D, int R>
 hipError_t go_decode_e(const sl::DsDecodeParams& p, int batch, hipStream_t s) {
   if (p.max_seq <= 8 * GT) return go_decode<D, R, 8>(p, batch, s);
+  if (p.max_seq <= 16 * GT) return go_decode<D, R, 16>(p, batch, s);
   return go_decode<D, R, 32>(p, batch, s);
 }
 

@@ -128,6 +128,17 @@ def test_decode_max_sequence(fas):
     _check(inp, 100, out, toks)
 
 
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_decode_sixteen_slot_layout(fas, r):
+    # 8192 < max_seq <= 16384: 16 scores per thread, two workgroups per CU
+    print(f"[ds] 16-slot layout r={r}", flush=True)
+    c = wda.DecodeCase("t", 2, 4, 128, 12000, r, 700, ragged=True, seed=21)
+    inp = wda.make_inputs(c)
+    inp.seq_len[0] = 12000
+    out, toks = _run(fas, inp, 700)
+    _check(inp, 700, out, toks)
+
+
 def test_label_cache_append(fas):
     # decode-style update: one token per sequence at a ragged position
     import torch
