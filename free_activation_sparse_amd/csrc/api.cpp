@@ -636,6 +636,8 @@ sl_status ds_decode_attention(const void* q, const void* key, const void* value,
     if (k < max_seq && k > DS_MAX_K)
       return fail(SL_ERR_UNSUPPORTED, "k=%d: at most %d kept tokens unless k >= max_seq", (int)k, DS_MAX_K);
     if (k < max_seq && label == nullptr) return fail(SL_ERR_ARG, "label must not be NULL when k < max_seq");
+    if (tokens_out != nullptr && k > DS_MAX_SEQ)
+      return fail(SL_ERR_ARG, "k=%d: tokens_out needs k <= %d", (int)k, DS_MAX_SEQ);
     if (!std::isfinite(scale)) return fail(SL_ERR_ARG, "scale must be finite");
     const size_t row_align = head_dim == 128 ? 16 : 8;
     if (!aligned(q, row_align) || !aligned(key, row_align) || !aligned(value, row_align))

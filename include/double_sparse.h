@@ -89,6 +89,7 @@ sl_status ds_label_cache_update(const void* key, void* label, const int32_t* cha
  *   out        device fp32 [batch][heads][head_dim]
  *   tokens_out device int32 [batch][heads][k] or NULL: the kept token indices
  *              in ascending order, then -1 for the k - |T| unused slots
+ *              (requires k <= DS_MAX_SEQ)
  *   head_dim 64 or 128; r 8, 16 or 32; 1 <= max_seq <= DS_MAX_SEQ;
  *   batch * heads <= 2^31 - 1. Alignment: q, key and value to 16 bytes
  *   (head_dim 128) or 8 bytes (64), label to 16 bytes (SL_ERR_UNSUPPORTED

@@ -155,6 +155,7 @@ def _ds(slib, q=_P, key=_P, value=_P, label=_P, ch=_P, sl=_P, B=2, H=4, S=128, d
     (dict(scale=float("inf")), 1), (dict(scale=float("nan")), 1),
     (dict(label=_P + 8), 2), (dict(q=_P + 8), 2), (dict(d=64, q=_P + 4), 2), (dict(out=_P + 2), 1),
     (dict(toks=_P + 2), 1), (dict(B=1 << 16, H=1 << 16), 1),
+    (dict(toks=_P, k=40000), 1),                                  # tokens_out with k above DS_MAX_SEQ
 ])
 def test_ds_decode_rejects(slib, kw, status):
     assert _ds(slib, **kw) == status
