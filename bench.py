@@ -100,7 +100,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the sparse linear is measured per GPU; see DESIGN.md for how it would shard)",
+              "(the sparse linear is measured on one GPU; split by output rows, each GPU would run the same "
+              "kernels on its own rows with no exchange before the product)",
               file=sys.stderr)
         sys.exit(2)
 
