@@ -397,7 +397,8 @@ def workload_legs(name):
         return [("block", 1, lins), ("grouped", 1, lins, groups)]
     if name == "phi4_ffn_stat":
         lins = [(4, li, dict(gate="stat", s_keep=0.10)) for li in range(3)]
-        return [(f"B{b}", b, lins) for b in (1, 2, 4, 8)]
+        # "B1_grouped": gate and up in one launch (gate's token for both), then down
+        return [(f"B{b}", b, lins) for b in (1, 2, 4, 8)] + [("B1_grouped", 1, lins, [[0, 1], [2]])]
     if name == "qwen_ffn_b16":
         legs = []
         for p in (0.65, 0.90):
