@@ -7,14 +7,16 @@
 //   1. Label stream: thread t scores tokens t, t + 1024, ... (E per thread,
 //      scores kept in registers as order-preserving 32-bit keys). Each token's
 //      r label values are one contiguous 16/32/64-byte run; a wavefront's
-//      loads cover 64 consecutive tokens.
+//      loads cover 64 consecutive tokens. All row loads of the kernel are
+//      non-temporal (every label, key and value row is read once per step).
 //   2. Select: the k-th largest key and the last kept tie's index, with the
 //      same machinery as the linear layer's top-K gate: a 4096-bin LDS
 //      histogram window below the largest key, exact ranking of the pivot
 //      bin's candidates by one wavefront, and a radix-select fallback on key
 //      digits (12/12/8 bits) then on the reversed index (8/7 bits).
-//   3. Compaction: ballots + a prefix over (slot, wavefront) counts write the
-//      kept token indices to LDS in ascending order.
+//   3. Compaction: ballots + a prefix over (slot, wavefront) counts, which
+//      every wavefront scans itself, write the kept token indices to LDS in
+//      ascending order.
 //   4. Attention: 16 lanes per token row (16 or 8 bytes of the key and value
 //      rows per lane), 64 rows per workgroup step, four steps of key and value
 //      loads in flight; each 16-lane row keeps its own online softmax (running

@@ -139,6 +139,25 @@ def test_decode_sixteen_slot_layout(fas, r):
     _check(inp, 700, out, toks)
 
 
+def test_decode_clamped_lengths_and_wrapped_channels(fas):
+    # documented error behaviour: lengths are clamped to [0, max_seq] and a
+    # channel index outside [0, head_dim) is taken modulo head_dim
+    import torch
+    print("[ds] clamped lengths / wrapped channels", flush=True)
+    c = wda.DecodeCase("t", 3, 2, 64, 200, 8, 30, seed=22)
+    inp = wda.make_inputs(c)
+    lens = np.array([500, -5, 150], np.int32)
+    wrapped = inp.channels + 64 * np.array([[0, 1, 2, 0, 3, 0, 1, 0]], np.int32)
+    q, K, V = _dev(inp.q, torch), _dev(inp.key, torch), _dev(inp.value, torch)
+    L = torch.empty((3, 2, 200, 8), dtype=torch.bfloat16, device="cuda")
+    chw = _dev(wrapped, torch)
+    fas.label_cache_update(K, L, chw)
+    out, toks = fas.decode_attention(q, K, V, L, chw, _dev(lens, torch), 30, tokens_out=True)
+    torch.cuda.synchronize()
+    inp.seq_len = np.clip(lens, 0, 200)
+    _check(inp, 30, out.cpu().numpy(), toks.cpu().numpy())
+
+
 def test_label_cache_append(fas):
     # decode-style update: one token per sequence at a ragged position
     import torch
