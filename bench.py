@@ -567,7 +567,9 @@ def run_ffn_chain(args):
                       "K": Ks, "weight_ring_copies": R},
            "kept_weight_bytes": kept_bytes, "dense_weight_bytes": dense_bytes,
            "kept_GBps": kept_bytes / (us * 1e-6) / 1e9, "launches_per_token": 3,
-           "data": "synthetic", "device": torch.cuda.get_device_name(0)}
+           "data": "synthetic", "device": torch.cuda.get_device_name(0),
+           "cpu_baseline": None if args.no_cpu else ffn_cpu_baseline(
+               host, Ks, wl.random_tokens(310, 8, n, "bf16", "normal"), min(args.cpu_seconds, 10.0))}
     print(json.dumps(out))
     for ring in rings:
         for h in ring:
@@ -689,6 +691,7 @@ def run_ds_decode(args):
                         "kernel": "ds_decode_kernel", "kernel_us": round(head["kernel_us"], 2),
                         "algorithmic_bytes": head["algorithmic_bytes"]},
            "legs": legs, "device": torch.cuda.get_device_name(0)}
+    res["cpu_baseline"] = None if args.no_cpu else ds_cpu_baseline(base, min(args.cpu_seconds, 10.0))
     print(json.dumps(res))
 
 
@@ -793,6 +796,68 @@ def cpu_baseline(wl, Wh, K, seconds):
     return {"value": round(done / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{done} tokens of the 4096x11008 bf16 layer at K={K} (fp64 numpy oracle: scores, "
                       f"lexsort top-K, gathered product), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return 1
+
+
+def ffn_cpu_baseline(host, Ks, tokens, seconds):
+    """The sparse-linear oracle through the FFN chain on the host, per token:
+    gate and up forwards, h = bf16(SiLU(g) u), down forward; bounded by
+    `seconds` (column norms precomputed, as the library does at init)."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    cs = [oracle.column_norms(W) for W in host]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        x = tokens[done % len(tokens)]
+        g = oracle.forward(host[0], cs[0], x, "topk", K=Ks[0])["y"]
+        u = oracle.forward(host[1], cs[1], x, "topk", K=Ks[1])["y"]
+        h = wl.f32_to_bf16_bits((g / (1.0 + np.exp(-g)) * u).astype(np.float32))
+        oracle.forward(host[2], cs[2], h, "topk", K=Ks[2])
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 64:
+            break
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{done} tokens through gate/up 11008x4096 and down 4096x11008 at K={Ks} (fp64 numpy "
+                      f"oracle per projection, numpy SiLU(g) u), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+
+
+def ds_cpu_baseline(case, seconds):
+    """The Double Sparsity oracle on the host, one (sequence, head) pair at a
+    time (label cache, fp32 label scores, lexsort top-k, fp64 attention),
+    bounded by `seconds`; reported per sequence (32 heads)."""
+    import numpy as np
+    from oracle import double_sparse as ods
+    from workloads import decode_attention as wda
+    inp = wda.make_inputs(case, batch=1)
+    S, k = case.max_seq, case.k
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        h = done % case.heads
+        lab = ods.label_cache(inp.key[:, h:h + 1], inp.channels[h:h + 1])[0, 0]
+        s = ods.approx_scores(inp.q[0, h], lab, inp.channels[h], S)
+        idx = ods.heavy_tokens(s, k)
+        ods.sparse_attention(inp.q[0, h], inp.key[0, h], inp.value[0, h], idx, case.head_dim ** -0.5)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= case.batch * case.heads:
+            break
+    return {"value": round(done / case.heads / el, 4), "unit": "sequences/s", "cores": _oracle_threads(),
+            "kind": "oracle",
+            "sample": f"{done} (sequence, head) pairs (the heads of one {S}-token sequence, repeated: as many "
+                      f"pairs as one batch-{case.batch} step) at r={case.r}, k={k} (numpy oracle: label cache, "
+                      f"fp32 label scores, lexsort top-k, fp64 attention), {el:.1f} s on {os.cpu_count()} host "
+                      f"CPUs visible; sequences/s = pairs/s / {case.heads} heads"}
 
 
 if __name__ == "__main__":
