@@ -511,7 +511,7 @@ def run_workload(args):
         "roofline": {"bound": "hbm", "achieved": round(head["product_GBps"], 1), "peak": PEAK_GBS,
                      "unit": "GB/s", "frac": round(head["product_GBps"] / PEAK_GBS, 4), "traffic": None,
                      "kernel": "product kernels of one step (summed bytes / summed durations)"},
-        "cpu_baseline": None,
+        "cpu_baseline": None if args.no_cpu else workload_cpu_baseline(legs[0], host_w, min(args.cpu_seconds, 10.0)),
         "legs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                  for k, v in results.items()},
         "device": torch.cuda.get_device_name(0),
@@ -804,6 +804,31 @@ def _oracle_threads():
         return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         return 1
+
+
+def workload_cpu_baseline(leg, host_w, seconds):
+    """The sparse-linear oracle on the host for a workload's first leg: tokens
+    one at a time through every linear of the leg (the union of a batch is an
+    execution detail, so the oracle's work per token is the same), bounded by
+    `seconds` (column norms precomputed)."""
+    import oracle
+    import workloads as wl
+    name, B, lins = leg[:3]
+    cs = {(cfg, li): oracle.column_norms(host_w[(cfg, li)]) for cfg, li, _ in lins}
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for cfg, li, gk in lins:
+            x = wl.token(cfg, li, done)
+            mode = gk["gate"]
+            oracle.forward(host_w[(cfg, li)], cs[(cfg, li)], x, mode, K=gk.get("K"), s_keep=gk.get("s_keep"))
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= 64:
+            break
+    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{done} tokens through the {len(lins)} linears of leg {name} (fp64 numpy oracle per "
+                      f"linear: scores, select, gathered product), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
 
 
 def ffn_cpu_baseline(host, Ks, tokens, seconds):
