@@ -158,6 +158,17 @@ def test_decode_clamped_lengths_and_wrapped_channels(fas):
     _check(inp, 30, out.cpu().numpy(), toks.cpu().numpy())
 
 
+@pytest.mark.parametrize("k", [999, 1000])
+def test_decode_boundary_k(fas, k):
+    # n = 1000 for every sequence: k = n - 1 drops exactly one token (the
+    # smallest score, ties to the highest index); k = n is the dense path
+    print(f"[ds] boundary k={k}", flush=True)
+    c = wda.DecodeCase("t", 2, 4, 128, 1000, 16, k, seed=24)
+    inp = wda.make_inputs(c)
+    out, toks = _run(fas, inp, k)
+    _check(inp, k, out, toks)
+
+
 def test_label_cache_append(fas):
     # decode-style update: one token per sequence at a ragged position
     import torch
