@@ -17,12 +17,17 @@ Every function restates, in plain slow code, what the pages define:
   index-list product): y accumulates x_j times the weight vector of input j
   over the active indices only.
 
+* Spark Transformer article, section 2.1 (the FFN scores, selects and
+  computes only the selected part): the sparse FFN chain gate/up -> h =
+  bf16(SiLU(g) u) -> down, each projection with its own gate
+  (``oracle.ffn``).
+
 * Double Sparsity article, section 在线前向计算 (online forward): decode
   attention over the tokens whose label-channel scores are the k largest
   (``oracle.double_sparse``).
 
-Parity status of each function is listed in ``oracle.sparse_linear`` and
-``oracle.double_sparse``.
+Parity status of each function is listed in ``oracle.sparse_linear``,
+``oracle.ffn`` and ``oracle.double_sparse``.
 """
 from .sparse_linear import (  # noqa: F401
     as_f64,
@@ -39,4 +44,6 @@ from .sparse_linear import (  # noqa: F401
     gate,
     forward,
 )
+from .ffn import silu, bf16_round, silu_mul, ffn_chain  # noqa: F401,E402
 from . import double_sparse  # noqa: F401,E402
+from . import ffn  # noqa: F401,E402

@@ -25,10 +25,19 @@ Definitions followed (pages cited by title and section):
 * ``sparse_product`` -- Spark Transformer article, section 3.1 (SVMM, the
   index-list product): y = sum over active j of x_j * W[:, j], in fp64.
 
+* ``gate(mode="fixed")`` -- WINA article, section 三 (per-layer thresholds
+  calibrated from hidden-state distributions): keep score > tau with tau
+  rounded to fp32 first; the reported threshold is that fp32 value.
+
 Parity pins (tests/test_oracle_*.py): brute-force pairwise dominance for the
 top-K set, hypothesis tie-heavy cases, closed forms for scores, norms and the
 statistical threshold, AS241 against mpmath, integer brute-force products,
-the orthogonal-column error identity and the WINA <= TEAL error inequality.
+the orthogonal-column error identity and the WINA <= TEAL error inequality;
+for the fixed threshold, a score equal to fp32(tau) dropped, tau rounded
+before the comparison, tau = 0 keeping exactly the nonzero scores, a tau above
+every score keeping nothing, and the count of a sorted copy above fp32(tau).
+Planted mistakes in each function fail these pins
+(tests/test_oracle_mutations.py).
 No page prints a worked numeric example, so no function is pinned to printed
 values; every function has at least one independent pin above.
 """

@@ -114,6 +114,54 @@ def test_full_channel_scores_match_exact_dot_products():
     assert decided >= 6
 
 
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_label_scores_exact_on_integer_inputs(r):
+    # integer query and keys in [-60, 60] (exact in bf16): every partial sum is
+    # an integer below 2^24, so fp32 accumulation is exact and the approximate
+    # score must equal the exact dot product of q and k over the r label
+    # channels, whatever the summation order; the kept set is then the exact
+    # top-k of those integers (ties to the lower index)
+    g = np.random.default_rng(100 + r)
+    H, S, d, k = 3, 200, 128, 23
+    q = g.integers(-60, 61, (H, d)).astype(np.float32)
+    key = g.integers(-60, 61, (H, S, d)).astype(np.float32)
+    ch = np.stack([g.permutation(d)[:r] for _ in range(H)]).astype(np.int32)
+    label = ds.label_cache(_bf16(key)[None], ch)[0]
+    for h in range(H):
+        exact = key[h][:, ch[h]].astype(np.int64) @ q[h][ch[h]].astype(np.int64)
+        s = ds.approx_scores(_bf16(q[h]), label[h], ch[h], S)
+        assert np.array_equal(s.astype(np.int64), exact) and np.all(s == exact)
+        order = sorted(range(S), key=lambda t: (-exact[t], t))
+        assert ds.heavy_tokens(s, k).tolist() == sorted(order[:k])
+
+
+@pytest.mark.parametrize("r", [8, 16, 32])
+def test_label_scores_within_bound_of_exact(r):
+    # Gaussian bf16 data (the benchmark's distribution): the fp32 score lies
+    # within the sequential-sum error bound of the exact fp64 dot product over
+    # the label channels, and the kept set equals the exact top-k wherever the
+    # gap at the k-th score exceeds twice that bound
+    c, inp = _case(2, 8, 400, 128, r, 40, 50 + r, ragged=False)
+    gamma = r * 2.0 ** -24 / (1 - r * 2.0 ** -24)
+    decided = 0
+    for b in range(2):
+        for h in range(8):
+            chh = inp.channels[h]
+            qd = ds.as_f64(inp.q[b, h])[chh]
+            Kd = ds.as_f64(inp.key[b, h])[:, chh]
+            exact = Kd @ qd
+            bound = gamma * (np.abs(Kd) @ np.abs(qd))
+            L = ds.label_cache(inp.key[b:b + 1], inp.channels)[0, h]
+            s = ds.approx_scores(inp.q[b, h], L, chh, 400).astype(np.float64)
+            assert np.all(np.abs(s - exact) <= bound)
+            srt = np.sort(exact)[::-1]
+            if srt[39] - srt[40] > 2 * bound.max():
+                decided += 1
+                want = np.sort(np.lexsort((np.arange(400), -exact))[:40])
+                assert np.array_equal(ds.heavy_tokens(s.astype(np.float32), 40), want)
+    assert decided >= 4
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_heavy_tokens_pairwise_dominance(seed):
     g = np.random.default_rng(seed)

@@ -162,3 +162,68 @@ def test_gate_end_to_end_small():
     out = oracle.gate(np.array([1, -4, 2, 0.5], np.float32), np.array([2, 1, 0.5, 8], np.float32),
                       "topk", K=3)
     assert out["idx"].tolist() == [0, 1, 3] and out["thresh"] == 2.0
+
+
+# ---------------------------------------------------------------- fixed threshold
+# A calibrated per-layer threshold (WINA article, section 三): keep score > tau,
+# tau taken as an fp32 value. Each case below has an answer that follows from
+# the definition alone, and a plausible mistake (>= for >, comparing against
+# the unrounded tau, reporting a different threshold) fails at least one.
+def _fixed(x, c, tau):
+    return oracle.gate(np.asarray(x, np.float32), np.asarray(c, np.float32), "fixed", tau=tau)
+
+
+def test_fixed_gate_strict_comparison():
+    # scores [2, 4, 1, 4]: a score exactly equal to tau is dropped
+    out = _fixed([1, -4, 2, 0.5], [2, 1, 0.5, 8], 2.0)
+    assert out["idx"].tolist() == [1, 3] and out["count"] == 2 and out["thresh"] == 2.0
+    out = _fixed([1, -4, 2, 0.5], [2, 1, 0.5, 8], 4.0)
+    assert out["count"] == 0 and out["thresh"] == 4.0
+
+
+def test_fixed_gate_rounds_tau_to_fp32_first():
+    one = np.float32(1.0)
+    below = float(np.nextafter(one, np.float32(0)))  # largest fp32 below 1
+    # tau just below 1.0 (as fp64) rounds to fp32 1.0, so a score of exactly
+    # 1.0 is dropped; compared unrounded, it would be kept
+    tau = 1.0 - 2.0 ** -30
+    assert float(np.float32(tau)) == 1.0
+    out = _fixed([1.0, below, 1.5], [1, 1, 1], tau)
+    assert out["idx"].tolist() == [2] and out["thresh"] == 1.0
+    # tau just above the fp32 value below 1 rounds down onto it: 1.0 is kept,
+    # the score equal to that fp32 value is not
+    tau = below + 2.0 ** -40
+    assert float(np.float32(tau)) == below
+    out = _fixed([1.0, below, 0.5], [1, 1, 1], tau)
+    assert out["idx"].tolist() == [0] and out["thresh"] == below
+
+
+def test_fixed_gate_zero_and_huge_tau():
+    g = np.random.default_rng(6)
+    x = g.standard_normal(500).astype(np.float32)
+    x[g.choice(500, 60, replace=False)] = 0.0
+    c = np.abs(g.standard_normal(500)).astype(np.float32)
+    c[:7] = 0.0
+    # tau = 0 keeps exactly the inputs with a nonzero score (x_j != 0 and c_j != 0)
+    out = _fixed(x, c, 0.0)
+    want = np.flatnonzero((x != 0) & (c != 0))
+    assert out["idx"].tolist() == want.tolist() and out["thresh"] == 0.0
+    # a tau above every score keeps nothing; the largest fp32 keeps nothing too
+    top = float(np.max(np.abs(x.astype(np.float64)) * c))
+    assert _fixed(x, c, 2 * top)["count"] == 0
+    assert _fixed(x, c, float(np.finfo(np.float32).max))["count"] == 0
+
+
+def test_fixed_gate_matches_sorted_count():
+    # the kept count equals the number of scores strictly above fp32(tau),
+    # counted from a sorted copy (searchsorted, a different routine)
+    g = np.random.default_rng(7)
+    for trial in range(20):
+        n = int(g.integers(1, 3000))
+        x = g.standard_normal(n).astype(np.float32)
+        c = np.abs(g.standard_normal(n)).astype(np.float32)
+        s = np.sort(np.abs(x) * c)  # numpy fp32 multiply: the IEEE scores
+        tau = float(s[int(g.integers(0, n))]) * float(g.choice([1.0, 1.0 + 2.0 ** -30, 0.999]))
+        out = _fixed(x, c, tau)
+        above = n - int(np.searchsorted(s, np.float32(tau), side="right"))
+        assert out["count"] == above
