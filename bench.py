@@ -1,24 +1,29 @@
 """Benchmark of the weight-informed activation-sparse linear on one MI355X.
 
-Workload: the Llama-2-7B-shaped FFN down projection, W 4096 x 11008 bf16
-(std 0.02), x = SiLU(g) * u with g, u ~ N(0, 1) rounded to bf16, one token per
-step (batch-1 decode), WINA top-K at 50 % sparsity (K = 5504, the headline) and
-65 % sparsity (K = 3853). A step is one full forward, one fused launch: a gate
-workgroup (scores, top-K select) and the product workgroups (predicate,
-compaction, gather-GEMV). The two-launch form (gate kernel, then product
-kernel) is timed beside it.
+Headline workload: the Llama-2-7B-shaped FFN down projection, W 4096 x 11008
+bf16 (std 0.02), x = SiLU(g) * u with g, u ~ N(0, 1) rounded to bf16, one
+token per step (batch-1 decode), WINA top-K at 50 % sparsity (K = 5504, the
+headline) and 65 % sparsity (K = 3853). A step is one full forward, one fused
+launch: a gate workgroup (scores, top-K select) and the product workgroups
+(predicate, compaction, gather-GEMV).
 
 Weights rotate through 12 handle-owned copies (1.08 GB) so the 256 MB
 Infinity Cache never serves them; tokens rotate through 256 seeded tokens held
-in HBM. Steps are captured into HIP graphs and replayed, so the host's per-call
-overhead does not throttle the GPU; the timed region is bracketed by
-torch.cuda.synchronize().
+in HBM. Before a leg is timed every ring copy runs once untimed (each copy's
+speculation starts from its own previous threshold, whatever --warmup is).
+Steps are captured into HIP graphs and replayed; the timed region is bracketed
+by torch.cuda.synchronize() and, inside it, by HIP events on the replay stream:
+tokens/s and ms per step come from the events (the wall clock of the bracket
+is reported beside them). The same-kernel dense forward is timed the same way,
+so speedup_vs_dense compares like with like; a kernel-to-kernel speed-up
+(average launch durations from HIP events around 600 back-to-back launches)
+is reported beside it.
 
 Printed: one JSON line with tokens/s, ms per step, the fused kernel's
-achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak (its
-duration from HIP events on its stream around back-to-back launches), the
-same-kernel dense baseline, hipBLASLt's dense GEMV for context, and the CPU
-oracle timed on the host.
+achieved HBM bandwidth on algorithmic bytes against the 8 TB/s peak, the
+same-kernel dense baseline, the practical gather ceiling (a read-only kernel
+streaming the same kept columns), hipBLASLt's dense GEMV for context, and the
+CPU oracle timed on the host at one thread and at all threads.
 """
 from __future__ import annotations
 
@@ -37,21 +42,21 @@ METRIC = "sparse-GEMV tokens/s & achieved HBM GB/s at 50%/65% sparsity, bf16"
 PEAK_GBS = 8000.0
 RING = 12
 NTOK = 256
+KERNEL_LAUNCHES = 600  # back-to-back launches per kernel-duration measurement
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=3000)
     ap.add_argument("--warmup", type=int, default=300)
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--only", choices=["sparse50", "sparse65", "fixed50", "dense", "all", "r8_k512", "r16_k256"],
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle budget (split between the one-thread and all-thread runs)")
+    ap.add_argument("--only", choices=["sparse50", "sparse65", "fixed50", "dense", "ceiling", "all", "r8_k512",
+                                       "r16_k256"],
                     default="all",
-                    help="restrict the measured legs (short profiler runs)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 256 MiB device copy (reference for memory counters)")
+                    help="restrict the measured legs (short profiler runs of one leg)")
     ap.add_argument("--counters-run", action="store_true",
                     help="short eager run for memory-counter passes: 12 + 48 headline forwards "
                          "(K=5504), then three plain 256 MiB device copies; prints one line")
@@ -59,7 +64,7 @@ def parse():
                     choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16", "llama2_ffn_chain",
                              "llama2_ds_decode"],
                     help="llama7b_down is the headline; the others measure the remaining layer shapes")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
 def algorithmic_bytes(m, n, K, B=1):
@@ -96,28 +101,96 @@ def traffic_from_profile(kernel, sources, K):
     return int(t.group(1)) if t else None
 
 
-def main():
-    args = parse()
+# ---------------------------------------------------------------------------
+# Timing helpers (f(i, stream) enqueues step i on the given HIP stream)
+# ---------------------------------------------------------------------------
+def _capture(torch, f, count, first=0):
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        for i in range(first, first + count):
+            f(i, s.cuda_stream)
+    return g
+
+
+def prime(torch, f, count):
+    """Untimed eager calls 0 .. count-1 (every ring copy and token slot once)."""
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(count):
+        f(i, s)
+    torch.cuda.synchronize()
+
+
+def timed_steps(torch, f, steps, warmup, G=120):
+    """Warm up, then time exactly `steps` calls of f replayed from HIP graphs
+    of up to G calls. Returns (seconds between HIP events recorded on the
+    replay stream around the timed replays, wall seconds of the
+    synchronize-bracketed region)."""
+    cache = {}
+
+    def graph_of(count):
+        if count not in cache:
+            cache[count] = _capture(torch, f, count)
+        return cache[count]
+    full, tail = divmod(steps, G)
+    wfull, wtail = divmod(warmup, G)
+    plan_warm = [G] * wfull + ([wtail] if wtail else [])
+    plan_timed = [G] * full + ([tail] if tail else [])
+    for cnt in set(plan_warm + plan_timed):
+        graph_of(cnt)
+    for cnt in plan_warm:
+        cache[cnt].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for cnt in plan_timed:
+        cache[cnt].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) * 1e-3, wall
+
+
+def graph_us(torch, f, count=KERNEL_LAUNCHES):
+    """Average microseconds per call of f, from HIP events on the replay
+    stream around one replay of a graph of `count` back-to-back calls (after
+    one untimed replay of the same graph)."""
+    g = _capture(torch, f, count)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / count
+
+
+def _r(v, nd=4):
+    return round(v, nd) if isinstance(v, float) else v
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the sparse linear is measured on one GPU; split by output rows, each GPU would run the same "
               "kernels on its own rows with no exchange before the product)",
               file=sys.stderr)
         sys.exit(2)
-
     if args.workload == "llama2_ffn_chain":
-        run_ffn_chain(args)
-        return
+        return run_ffn_chain(args)
     if args.workload == "llama2_ds_decode":
-        run_ds_decode(args)
-        return
+        return run_ds_decode(args)
     if args.workload != "llama7b_down":
-        run_workload(args)
-        return
+        return run_workload(args)
     if args.counters_run:
-        counters_run()
-        return
+        return counters_run()
+    return run_headline(args)
 
+
+def run_headline(args):
     import numpy as np
     import torch
 
@@ -134,14 +207,36 @@ def main():
     Ks = {"sparse50": wl.k_from_sparsity(n, 0.5), "sparse65": wl.k_from_sparsity(n, 0.65)}
     Y = torch.empty((RING, m), dtype=torch.float32, device=dev)
 
-    def make_ring(K):
-        return [fas.SparseLinear(Wd, c=None, gate="topk", K=K) for _ in range(RING)]
+    def make_ring(**gate):
+        return [fas.SparseLinear(Wd, c=None, **gate) for _ in range(RING)]
+
+    def layer_step(ring, dense=False):
+        """f(i, stream): forward of token i % 256 through ring copy i % 12."""
+        def f(i, s):
+            h, x, y = ring[i % RING], X[i % NTOK], Y[i % RING]
+            if dense:
+                fas.sparse_linear_forward_dense(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32, s)
+            else:
+                fas.sparse_linear_forward(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32, 0, 0, 0, s)
+        return f
+
+    def stage_step(ring, bit):
+        def f(i, s):
+            k = i % RING
+            fas.sparse_linear_forward_stages(ring[k].handle, X[k].data_ptr(), 1, Y[k].data_ptr(), fas.SL_F32,
+                                             0, 0, 0, bit, s)
+        return f
+
+    def sync_all(ring):
+        for h in ring:
+            h.sync_status()  # raises if a fused hand-off timed out in any timed call
 
     # Fixed (calibrated) threshold leg: tau = the median score over the 256
-    # tokens (c from the library; plain numpy on the host, outside any timed
-    # region), so that about half of each token's inputs are kept
+    # tokens (scores from the library's norms; plain numpy on the host, outside
+    # any timed region), so that about half of each token's inputs are kept
     fixed_tau, fixed_kept = None, None
-    if args.only in ("all", "fixed50"):
+    want = {"all": ("sparse50", "sparse65", "fixed50", "dense", "ceiling")}.get(args.only, (args.only,))
+    if "fixed50" in want:
         probe = fas.SparseLinear(Wd, c=None, gate="topk", K=1)
         c_host = probe.norms().cpu().numpy().astype(np.float64)
         probe.close()
@@ -150,127 +245,43 @@ def main():
         fixed_tau = float(np.median(sc))
         fixed_kept = float((sc > np.float32(fixed_tau)).sum(axis=1).mean())
 
-    def layer_step(ring, dense):
-        """f(i, stream): forward of token i % 256 through ring copy i % 12."""
-        def f(i, s):
-            h, x, y = ring[i % RING], X[i % NTOK], Y[i % RING]
-            if dense:
-                fas.sparse_linear_forward_dense(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32,
-                                                s.cuda_stream)
-            else:
-                fas.sparse_linear_forward(h.handle, x.data_ptr(), 1, y.data_ptr(), fas.SL_F32, 0, 0, 0,
-                                          s.cuda_stream)
-        return f
-
-    def run_steps(f, steps, warmup):
-        """Warm up, then time exactly `steps` calls of f; returns seconds. In
-        graph mode the calls are captured in chunks of 120 and replayed."""
-        if args.mode == "eager":
-            s = torch.cuda.current_stream()
-            for i in range(warmup):
-                f(i, s)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for i in range(steps):
-                f(i, s)
-            torch.cuda.synchronize()
-            return time.perf_counter() - t0
-        G = RING * 10
-        cache = {}
-
-        def graph_of(count):
-            if count not in cache:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    s = torch.cuda.current_stream()
-                    for i in range(count):
-                        f(i, s)
-                cache[count] = g
-            return cache[count]
-
-        full, tail = divmod(steps, G)
-        wfull, wtail = divmod(warmup, G)
-        plan_warm = [G] * wfull + ([wtail] if wtail else [])
-        plan_timed = [G] * full + ([tail] if tail else [])
-        for cnt in set(plan_warm + plan_timed):
-            graph_of(cnt)
-        for cnt in plan_warm:
-            cache[cnt].replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for cnt in plan_timed:
-            cache[cnt].replay()
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0
-
-    def time_graph(fn, count=600):
-        """Average microseconds per call of fn(i, stream), from HIP events on the
-        replay stream around one replay of a graph holding `count` calls
-        back to back."""
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            s = torch.cuda.current_stream()
-            for i in range(count):
-                fn(i, s)
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / count
-
-    def kernel_times(ring, dense):
-        """(gate us, product us, fused us, two-launch us). The fused launch and
-        the two-launch forward are timed whole; the gate and product kernels of
-        the two-launch form are also launched alone, back to back (ring copy i
-        keeps the selection of token i, so the product-only launches move
-        exactly the bytes of a full forward)."""
-        if dense:
-            return 0.0, time_graph(layer_step(ring, True)), None, None
-        fused_us = time_graph(layer_step(ring, False))
-        for h in ring:
-            h.set_fused(False)
-        two_us = time_graph(layer_step(ring, False))
-        s0 = torch.cuda.current_stream()
-        for i in range(RING):
-            fas.sparse_linear_forward(ring[i].handle, X[i].data_ptr(), 1, Y[i].data_ptr(), fas.SL_F32,
-                                      0, 0, 0, s0.cuda_stream)
-
-        def stage(bit):
-            def f(i, s):
-                k = i % RING
-                fas.sparse_linear_forward_stages(ring[k].handle, X[k].data_ptr(), 1, Y[k].data_ptr(),
-                                                 fas.SL_F32, 0, 0, 0, bit, s.cuda_stream)
-            return f
-        gate_us = time_graph(stage(fas.SL_STAGE_GATE))
-        prod_us = time_graph(stage(fas.SL_STAGE_PRODUCT))
-        for h in ring:
-            h.set_fused(True)
-        return gate_us, prod_us, fused_us, two_us
-
     results = {}
-    legs = ["sparse50", "sparse65", "fixed50"] if args.only == "all" else ([args.only] if args.only != "dense" else [])
-    for leg in legs:
+    for leg in ("sparse50", "sparse65", "fixed50"):
+        if leg not in want:
+            continue
         if leg == "fixed50":
             K = fixed_kept  # mean kept count over the tokens (algorithmic bytes)
-            ring = [fas.SparseLinear(Wd, c=None, gate="fixed", tau=fixed_tau) for _ in range(RING)]
+            ring = make_ring(gate="fixed", tau=fixed_tau)
         else:
             K = Ks[leg]
-            ring = make_ring(K)
-        secs = run_steps(layer_step(ring, False), args.steps, args.warmup)
-        gate_us, prod_us, fused_us, two_us = kernel_times(ring, False)
+            ring = make_ring(gate="topk", K=K)
+        step = layer_step(ring)
+        prime(torch, step, 2 * RING)
+        ev, wall = timed_steps(torch, step, args.steps, args.warmup)
+        fused_us = graph_us(torch, step)
+        sync_all(ring)
+        # the two-launch form (gate kernel, then product kernel), and each of
+        # its kernels alone (ring copy i keeps the selection of token i, so the
+        # product-only launches move exactly the bytes of a full forward)
         for h in ring:
-            h.sync_status()
+            h.set_fused(False)
+        two_us = graph_us(torch, step)
+        prime(torch, step, RING)
+        gate_us = None
+        if leg != "fixed50":  # a fixed threshold without outputs launches no gate kernel
+            gate_us = graph_us(torch, stage_step(ring, fas.SL_STAGE_GATE))
+        prod_us = graph_us(torch, stage_step(ring, fas.SL_STAGE_PRODUCT))
+        for h in ring:
+            h.set_fused(True)
         ab = algorithmic_bytes(m, n, K)
         results[leg] = {
             "K": K, "sparsity": 1 - K / n,
             **({"tau": fixed_tau, "gate": "fixed threshold (median score of the 256 tokens)"} if leg == "fixed50" else {}),
-            "tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
+            "tokens_per_s": args.steps / ev, "us_per_step": ev / args.steps * 1e6,
+            "wall_us_per_step": wall / args.steps * 1e6,
             "fused_kernel_us": fused_us, "algorithmic_bytes": ab,
             "fused_achieved_GBps": ab / (fused_us * 1e-6) / 1e9,
-            "step_achieved_GBps": ab / (secs / args.steps) / 1e9,
+            "step_achieved_GBps": ab / (ev / args.steps) / 1e9,
             "two_launch_us_per_step": two_us,
             "gate_kernel_us": gate_us, "product_kernel_us": prod_us,
             "product_achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
@@ -280,22 +291,25 @@ def main():
         del ring
 
     dense = None
-    if args.only in ("all", "dense"):
-        ring = make_ring(Ks["sparse50"])
-        secs = run_steps(layer_step(ring, True), args.steps, args.warmup)
-        _, prod_us, _, _ = kernel_times(ring, True)
+    if "dense" in want:
+        ring = make_ring(gate="topk", K=Ks["sparse50"])
+        step = layer_step(ring, dense=True)
+        prime(torch, step, RING)
+        ev_a, wall_a = timed_steps(torch, step, args.steps, args.warmup)
+        k_a = graph_us(torch, step)
         # the ordered split reduction needs no clearing of y (no fill kernel
-        # before the product): the speedup is taken against the faster form
+        # before the product): the speed-ups are taken against the faster form
         for h in ring:
             h.set_deterministic(True)
-        ordered_us = time_graph(layer_step(ring, True))
+        ev_o, wall_o = timed_steps(torch, step, args.steps, args.warmup)
+        k_o = graph_us(torch, step)
         for h in ring:
             h.set_deterministic(False)
         ab = algorithmic_bytes(m, n, n)
-        best_us = min(secs / args.steps * 1e6, ordered_us)
-        dense = {"tokens_per_s": args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
-                 "product_kernel_us": prod_us, "achieved_GBps": ab / (prod_us * 1e-6) / 1e9,
-                 "ordered_reduction_us_per_step": ordered_us, "best_us_per_step": best_us}
+        dense = {"us_per_step_atomic": ev_a / args.steps * 1e6, "us_per_step_ordered": ev_o / args.steps * 1e6,
+                 "launch_us_atomic": k_a, "launch_us_ordered": k_o,
+                 "best_us_per_step": min(ev_a, ev_o) / args.steps * 1e6, "best_launch_us": min(k_a, k_o),
+                 "algorithmic_bytes": ab, "achieved_GBps": ab / (min(k_a, k_o) * 1e-6) / 1e9}
         for h in ring:
             h.close()
         del ring
@@ -305,10 +319,10 @@ def main():
 
         def mv(i):
             torch.matmul(Wr[i % RING], X[i % NTOK], out=Yb[i % RING])
-        for i in range(args.warmup):
+        for i in range(2 * RING):
             mv(i)
-        # hipBLASLt calls cannot be captured in a graph: time them eagerly between
-        # two events, with the GPU first asleep so the host runs ahead
+        # hipBLASLt calls are not captured in a graph here: time them eagerly
+        # between two events, with the GPU first asleep so the host runs ahead
         count = 1200
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
@@ -318,24 +332,43 @@ def main():
             mv(i)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / count
-        dense["torch_matmul_us_per_step"] = us
-        dense["torch_matmul_tokens_per_s"] = 1e6 / us
+        dense["torch_matmul_us_per_step"] = e0.elapsed_time(e1) * 1e3 / count
         del Wr
 
-    if args.copy_calibration:
-        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
+    ceiling = {}
+    if "ceiling" in want:
+        # the practical ceiling: a read-only kernel streaming each token's own
+        # kept columns (the masks come from the library's forward, untimed)
+        sink = torch.zeros(1, dtype=torch.float32, device=dev)
+        for leg, K in Ks.items():
+            ring = make_ring(gate="topk", K=K)
+            mk = torch.empty((RING, n), dtype=torch.uint8, device=dev)
+            s0 = torch.cuda.current_stream().cuda_stream
+            for r in range(RING):
+                fas.sparse_linear_forward(ring[r].handle, X[r].data_ptr(), 1, Y[r].data_ptr(), fas.SL_F32,
+                                          mk[r].data_ptr(), 0, 0, s0)
+            torch.cuda.synchronize()
+            idx = [torch.nonzero(mk[r]).flatten().to(torch.int32).contiguous() for r in range(RING)]
+            counts = [int(t.numel()) for t in idx]
+            assert all(c == K for c in counts), counts
+
+            def gath(i, s, ring=ring, idx=idx):
+                r = i % RING
+                fas.sparse_linear_gather_ceiling(ring[r].handle, idx[r].data_ptr(), idx[r].numel(), sink.data_ptr(), s)
+            us = graph_us(torch, gath)
+            kept_bytes = K * m * 2
+            ceiling[leg] = {"K": K, "launch_us": us, "kept_weight_bytes": kept_bytes,
+                            "achieved_GBps": kept_bytes / (us * 1e-6) / 1e9,
+                            "frac_of_peak": kept_bytes / (us * 1e-6) / 1e9 / PEAK_GBS}
+            for h in ring:
+                h.close()
+            del ring
 
     cpu = None
     if not args.no_cpu and "sparse50" in results:
         cpu = cpu_baseline(wl, Wh, Ks["sparse50"], args.cpu_seconds)
 
-    head = results.get("sparse50") or results.get("sparse65")
+    head = results.get("sparse50") or results.get("sparse65") or results.get("fixed50")
     out = {
         "metric": METRIC,
         "value": head["tokens_per_s"] if head else None,
@@ -343,7 +376,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"] if head else None,
+        "ms_per_step": head["us_per_step"] * 1e-3 if head else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -352,29 +385,36 @@ def main():
         "config": {"workload": "llama2_7b_down_proj_4096x11008_bf16_topk_50pct",
                    "m": m, "n": n, "K": Ks["sparse50"], "batch": 1, "tokens": NTOK,
                    "weight_ring_copies": RING, "weight_ring_bytes": RING * m * n * 2,
-                   "launch": args.mode},
+                   "launch": "graph", "timing": "HIP events around the timed graph replays"},
     }
     if head:
+        out["wall_ms_per_step"] = head["wall_us_per_step"] * 1e-3
+        K0 = head["K"]
         out["roofline"] = {
             "bound": "hbm",
             "achieved": round(head["fused_achieved_GBps"], 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(head["fused_achieved_GBps"] / PEAK_GBS, 4),
-            "traffic": traffic_from_profile("fused_kernel", FUSED_SOURCES, Ks["sparse50"]),
+            "traffic": traffic_from_profile("fused_kernel", FUSED_SOURCES, K0) if isinstance(K0, int) else None,
             "kernel": "fused_kernel (gate workgroup + gather-GEMV workgroups)",
             "kernel_us": round(head["fused_kernel_us"], 3),
             "algorithmic_bytes": head["algorithmic_bytes"],
         }
     out["cpu_baseline"] = cpu
-    out["legs"] = {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                   for k, v in results.items()}
+    out["legs"] = {k: {kk: _r(vv) for kk, vv in v.items()} for k, v in results.items()}
     if dense:
-        out["dense_same_kernel"] = {k: round(v, 4) for k, v in dense.items()}
+        out["dense_same_kernel"] = {k: _r(v) for k, v in dense.items()}
         for k, v in results.items():
             bar = 0.8 / (1 - v["sparsity"])
-            out["legs"][k]["speedup_vs_dense"] = round(v["tokens_per_s"] * dense["best_us_per_step"] * 1e-6, 4)
+            out["legs"][k]["speedup_vs_dense"] = round(dense["best_us_per_step"] / v["us_per_step"], 4)
+            out["legs"][k]["kernel_speedup_vs_dense"] = round(dense["best_launch_us"] / v["fused_kernel_us"], 4)
             out["legs"][k]["speedup_bar"] = round(bar, 4)
+    if ceiling:
+        out["gather_ceiling"] = {k: {kk: _r(vv) for kk, vv in v.items()} for k, v in ceiling.items()}
+        for k, v in ceiling.items():
+            if k in results:
+                out["legs"][k]["fused_vs_ceiling"] = round(v["launch_us"] / results[k]["fused_kernel_us"], 4)
     out["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(out))
 
@@ -384,7 +424,7 @@ def main():
 # a batch of B tokens (ring copies of the weights so that >= 1 GiB rotates).
 # ---------------------------------------------------------------------------
 def workload_legs(name):
-    """[(leg name, B, [(cfg, linear, gate kwargs), ...])]"""
+    """[(leg name, B, [(cfg, linear, gate kwargs), ...], groups or None)]"""
     import workloads as wl
     if name == "llama3_block":
         ps = wl.component_sparsities(3)
@@ -394,17 +434,17 @@ def workload_legs(name):
         # (q, k, v | o | gate, up | down: 4 launches instead of 7)
         names = [l.name for l in wl.CONFIGS[3].linears]
         groups = [[names.index(a) for a in g] for g in (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))]
-        return [("block", 1, lins), ("grouped", 1, lins, groups)]
+        return [("grouped", 1, lins, groups), ("block", 1, lins, None)]
     if name == "phi4_ffn_stat":
         lins = [(4, li, dict(gate="stat", s_keep=0.10)) for li in range(3)]
         # "B1_grouped": gate and up in one launch (gate's token for both), then down
-        return [(f"B{b}", b, lins) for b in (1, 2, 4, 8)] + [("B1_grouped", 1, lins, [[0, 1], [2]])]
+        return [("B1_grouped", 1, lins, [[0, 1], [2]])] + [(f"B{b}", b, lins, None) for b in (1, 2, 4, 8)]
     if name == "qwen_ffn_b16":
         legs = []
         for p in (0.65, 0.90):
             lins = [(5, li, dict(gate="topk", K=wl.k_from_sparsity(wl.CONFIGS[5].linears[li].n, p)))
                     for li in range(3)]
-            legs.append((f"p{int(p * 100)}", 16, lins))
+            legs.append((f"p{int(p * 100)}", 16, lins, None))
         return legs
     raise ValueError(name)
 
@@ -426,9 +466,7 @@ def run_workload(args):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     results = {}
-    for spec in legs:
-        leg, B, lins = spec[:3]
-        groups = spec[3] if len(spec) > 3 else None
+    for leg, B, lins, groups in legs:
         total = sum(wl.CONFIGS[cfg].linears[li].m * wl.CONFIGS[cfg].linears[li].n * 2 for cfg, li, _ in lins)
         R = max(2, -(-(1 << 30) // total))
         rings, Xs, Ys, dims = [], [], [], []
@@ -443,58 +481,96 @@ def run_workload(args):
             Xs.append(dev_bf16(toks).reshape(NT, B, lin.n).contiguous())
             Ys.append(torch.empty((R, B, lin.m), dtype=torch.float32, device=dev))
             dims.append((lin.name, lin.m, lin.n))
+        # launch units: groups of linears sharing x (one launch each), or one
+        # linear per unit
+        units = groups if groups is not None else [[L] for L in range(len(lins))]
 
-        def step(i, s, stages=3):
-            if groups is not None:
-                # one token: a group's linears share x (the token of its first linear)
-                for g in groups:
-                    fas.sparse_linear_forward_group([rings[L][i % R].handle for L in g], Xs[g[0]][i % NT].data_ptr(),
-                                                    [Ys[L][i % R].data_ptr() for L in g], fas.SL_F32, s.cuda_stream)
-                return
-            for L in range(len(lins)):
-                h = rings[L][i % R]
-                fas.sparse_linear_forward_stages(h.handle, Xs[L][i % NT].data_ptr(), B, Ys[L][i % R].data_ptr(),
-                                                 fas.SL_F32, 0, 0, 0, stages, s.cuda_stream)
+        def unit_step(u, dense=False):
+            def f(i, s):
+                if len(u) > 1 and not dense:
+                    # one token: a group's linears share x (the token of its first linear)
+                    fas.sparse_linear_forward_group([rings[L][i % R].handle for L in u], Xs[u[0]][i % NT].data_ptr(),
+                                                    [Ys[L][i % R].data_ptr() for L in u], fas.SL_F32, s)
+                    return
+                for L in u:
+                    h = rings[L][i % R]
+                    x = Xs[u[0] if groups is not None else L][i % NT].data_ptr()
+                    if dense:
+                        fas.sparse_linear_forward_dense(h.handle, x, B, Ys[L][i % R].data_ptr(), fas.SL_F32, s)
+                    else:
+                        fas.sparse_linear_forward(h.handle, x, B, Ys[L][i % R].data_ptr(), fas.SL_F32, 0, 0, 0, s)
+            return f
 
-        secs = _replay_timed(torch, step, args.steps, args.warmup)
-        # untimed side pass: kept (B = 1) or union (B > 1) column counts per linear
+        def step_of(dense):
+            fs = [unit_step(u, dense) for u in units]
+
+            def f(i, s):
+                for g in fs:
+                    g(i, s)
+            return f
+
+        step = step_of(False)
+        prime(torch, step, 2 * R)
+        ev, wall = timed_steps(torch, step, args.steps, args.warmup, G=60)
+        unit_us = [graph_us(torch, unit_step(u), count=240) for u in units]
+        for ring in rings:
+            for h in ring:
+                h.sync_status()
+        dstep = step_of(True)
+        prime(torch, dstep, R)
+        dsteps = max(20, args.steps // 4)
+        dev_s, _ = timed_steps(torch, dstep, dsteps, min(args.warmup, dsteps), G=60)
+        dense_unit_us = [graph_us(torch, unit_step(u, True), count=120) for u in units]
+        # untimed side pass: kept (B = 1) or union (B > 1) column counts per
+        # linear, from the library's masks (one token batch per ring copy)
         kept = []
         for L, (name, m, n) in enumerate(dims):
             mk = torch.empty((B, n), dtype=torch.uint8, device=dev)
             tot = 0
+            x_of = (lambda t: Xs[[u for u in units if L in u][0][0]][t]) if groups is not None else (lambda t: Xs[L][t])
             for t in range(NT):
-                fas.sparse_linear_forward(rings[L][0].handle, Xs[L][t].data_ptr(), B, Ys[L][0].data_ptr(),
+                fas.sparse_linear_forward(rings[L][0].handle, x_of(t).data_ptr(), B, Ys[L][0].data_ptr(),
                                           fas.SL_F32, mk.data_ptr(), 0, 0, torch.cuda.current_stream().cuda_stream)
                 tot += int(mk.bool().any(dim=0).sum().item())
             kept.append(tot / NT)
-        # per-linear kernel times: ring copy r keeps the selection of token batch r
-        prod_us, gate_us = [], []
-        for L in range(len(lins)):
-            s0 = torch.cuda.current_stream()
-            for r in range(R):
-                fas.sparse_linear_forward(rings[L][r].handle, Xs[L][r].data_ptr(), B, Ys[L][r].data_ptr(),
-                                          fas.SL_F32, 0, 0, 0, s0.cuda_stream)
-
-            def one(bit, L=L):
-                def f(i, s):
-                    r = i % R
-                    fas.sparse_linear_forward_stages(rings[L][r].handle, Xs[L][r].data_ptr(), B,
-                                                     Ys[L][r].data_ptr(), fas.SL_F32, 0, 0, 0, bit, s.cuda_stream)
-                return f
-            gate_us.append(_graph_us(torch, one(fas.SL_STAGE_GATE)))
-            prod_us.append(_graph_us(torch, one(fas.SL_STAGE_PRODUCT)))
-        lin_rows = []
-        tot_bytes = 0
+        lin_rows, unit_rows = [], []
+        tot_bytes, touched_w = 0, 0
+        lin_bytes = []
         for L, (name, m, n) in enumerate(dims):
             ab = kept[L] * m * 2 + B * n * 2 + n * 4 + B * m * 4
+            lin_bytes.append(ab)
             tot_bytes += ab
+            touched_w += kept[L] * m * 2
             lin_rows.append({"linear": name, "m": m, "n": n, "columns_read": round(kept[L], 1),
-                             "gate_us": round(gate_us[L], 3), "product_us": round(prod_us[L], 3),
-                             "product_GBps": round(ab / (prod_us[L] * 1e-6) / 1e9, 1)})
-        results[leg] = {"B": B, "tokens_per_s": B * args.steps / secs, "ms_per_step": secs / args.steps * 1e3,
-                        "product_us_sum": sum(prod_us), "product_bytes_sum": tot_bytes,
-                        "product_GBps": tot_bytes / (sum(prod_us) * 1e-6) / 1e9,
-                        "dense_weight_bytes": total, "ring_copies": R, "linears": lin_rows}
+                             "column_density": round(kept[L] / n, 4)})
+        for ui, u in enumerate(units):
+            ub = sum(lin_bytes[L] for L in u)
+            unit_rows.append({"linears": [dims[L][0] for L in u], "launch_us": round(unit_us[ui], 3),
+                              "dense_launch_us": round(dense_unit_us[ui], 3),
+                              "algorithmic_bytes": round(ub),
+                              "achieved_GBps": round(ub / (unit_us[ui] * 1e-6) / 1e9, 1)})
+        us_step = ev / args.steps * 1e6
+        dense_us_step = dev_s / dsteps * 1e6
+        density = touched_w / total
+        kernel = ("fused_group_kernel" if groups is not None else "fused_kernel") if B == 1 else \
+            "gate_kernel + union_kernel (per linear)"
+        res = {"B": B, "tokens_per_s": B * args.steps / ev, "us_per_step": us_step,
+               "wall_us_per_step": wall / args.steps * 1e6,
+               "launch_us_sum": sum(unit_us), "algorithmic_bytes": tot_bytes,
+               "achieved_GBps": tot_bytes / (sum(unit_us) * 1e-6) / 1e9, "kernel": kernel,
+               "dense_same_kernel_us_per_step": dense_us_step,
+               "speedup_vs_dense": dense_us_step / us_step,
+               "kernel_speedup_vs_dense": sum(dense_unit_us) / sum(unit_us),
+               "dense_weight_bytes": total, "touched_weight_bytes": round(touched_w),
+               "touched_density": density, "ring_copies": R, "linears": lin_rows, "launches": unit_rows}
+        if B == 1:
+            res["speedup_bar"] = 0.8 / density  # 0.8 x dense / touched bytes
+        else:
+            # iid tokens keep 1 - (1 - f)^B of the columns between them: the
+            # union bound caps any speed-up at dense / touched bytes
+            res["union_bound"] = 1.0 / density
+            res["speedup_vs_union_bound"] = (dense_us_step / us_step) / (1.0 / density)
+        results[leg] = res
         for ring in rings:
             for h in ring:
                 h.close()
@@ -505,15 +581,15 @@ def run_workload(args):
     head = results[first]
     out = {
         "metric": METRIC, "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["us_per_step"] * 1e-3,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic", "config": {"workload": args.workload, "headline_leg": first, "launch": "graph"},
-        "roofline": {"bound": "hbm", "achieved": round(head["product_GBps"], 1), "peak": PEAK_GBS,
-                     "unit": "GB/s", "frac": round(head["product_GBps"] / PEAK_GBS, 4), "traffic": None,
-                     "kernel": "product kernels of one step (summed bytes / summed durations)"},
+        "data": "synthetic", "config": {"workload": args.workload, "headline_leg": first, "launch": "graph",
+                                        "timing": "HIP events around the timed graph replays"},
+        "roofline": {"bound": "hbm", "achieved": round(head["achieved_GBps"], 1), "peak": PEAK_GBS,
+                     "unit": "GB/s", "frac": round(head["achieved_GBps"] / PEAK_GBS, 4), "traffic": None,
+                     "kernel": head["kernel"] + " (summed algorithmic bytes / summed launch durations of one step)"},
         "cpu_baseline": None if args.no_cpu else workload_cpu_baseline(legs[0], host_w, min(args.cpu_seconds, 10.0)),
-        "legs": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                 for k, v in results.items()},
+        "legs": {k: {kk: _r(vv) for kk, vv in v.items()} for k, v in results.items()},
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out))
@@ -553,18 +629,20 @@ def run_ffn_chain(args):
         r = i % R
         fas.sparse_linear_forward_ffn(rings[0][r].handle, rings[1][r].handle, rings[2][r].handle,
                                       X[i % NT].data_ptr(), Y[r].data_ptr(), fas.SL_F32, WS[r].data_ptr(),
-                                      WS.shape[1], s.cuda_stream)
-    secs = _replay_timed(torch, step, args.steps, args.warmup)
+                                      WS.shape[1], s)
+    prime(torch, step, 2 * R)
+    ev, wall = timed_steps(torch, step, args.steps, args.warmup, G=60)
     for ring in rings:
         for h in ring:
             h.sync_status()
     kept_bytes = sum(K * a * 2 for K, (a, b) in zip(Ks, shapes))
     dense_bytes = sum(a * b * 2 for a, b in shapes)
-    us = secs / args.steps * 1e6
+    us = ev / args.steps * 1e6
     out = {"metric": "sparse FFN chain tokens/s (Llama-2-7B FFN shapes, top-K 50 % per projection)",
-           "value": args.steps / secs, "unit": "tokens/s", "ms_per_step": us * 1e-3,
+           "value": args.steps / ev, "unit": "tokens/s", "ms_per_step": us * 1e-3,
+           "wall_ms_per_step": wall / args.steps * 1e3,
            "config": {"workload": "llama2_7b_ffn_chain_gate_up_11008x4096_down_4096x11008_bf16_topk_50pct",
-                      "K": Ks, "weight_ring_copies": R},
+                      "K": Ks, "weight_ring_copies": R, "timing": "HIP events around the timed graph replays"},
            "kept_weight_bytes": kept_bytes, "dense_weight_bytes": dense_bytes,
            "kept_GBps": kept_bytes / (us * 1e-6) / 1e9, "launches_per_token": 3,
            "data": "synthetic", "device": torch.cuda.get_device_name(0),
@@ -657,34 +735,36 @@ def run_ds_decode(args):
             j = i % R
             fas.ds_decode_attention(Q.data_ptr(), Ks[j].data_ptr(), Vs[j].data_ptr(),
                                     Ls[j].data_ptr() if Ls else 0, ch.data_ptr(), sl.data_ptr(), B, H, S, d, r, k,
-                                    scale, out[j].data_ptr(), 0, s.cuda_stream)
+                                    scale, out[j].data_ptr(), 0, s)
         steps = args.steps if k < S else max(20, args.steps // 10)
-        secs = _replay_timed(torch, step, steps, min(args.warmup, steps))
-        kus = _graph_us(torch, step, count=120 if k < S else 30)
+        ev, wall = timed_steps(torch, step, steps, min(args.warmup, steps), G=60)
+        kus = graph_us(torch, step, count=120 if k < S else 30)
         nbytes = ds_algorithmic_bytes(B, H, S, d, r, k)
-        legs[name] = {"r": r, "k": k, "us_per_step": secs / steps * 1e6, "kernel_us": kus,
-                      "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (kus * 1e-6) / 1e9,
-                      "sequences_per_s": B * steps / secs}
+        legs[name] = {"r": r, "k": k, "us_per_step": ev / steps * 1e6, "wall_us_per_step": wall / steps * 1e6,
+                      "kernel_us": kus, "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (kus * 1e-6) / 1e9,
+                      "sequences_per_s": B * steps / ev}
         if Ls:
             # decode append: the newest token of every sequence (position seq_len - 1)
             upd = lambda i, s, L=Ls[0], ch=ch, r=r: fas.ds_label_cache_update(
-                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), last.data_ptr(), B, H, S, d, r, 1, s.cuda_stream)
-            legs[name]["label_append_us"] = _graph_us(torch, upd, count=120)
+                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), last.data_ptr(), B, H, S, d, r, 1, s)
+            legs[name]["label_append_us"] = graph_us(torch, upd, count=120)
             pre = lambda i, s, L=Ls[0], ch=ch, r=r: fas.ds_label_cache_update(
-                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), 0, B, H, S, d, r, S, s.cuda_stream)
-            legs[name]["label_prefill_us"] = _graph_us(torch, pre, count=20)
+                Ks[0].data_ptr(), L.data_ptr(), ch.data_ptr(), 0, B, H, S, d, r, S, s)
+            legs[name]["label_prefill_us"] = graph_us(torch, pre, count=20)
         del Ls
     head = legs.get("r8_k512") or next(iter(legs.values()))
     for name in ("r8_k512", "r16_k256"):
         if name in legs and "dense" in legs:
-            legs[name]["speedup_vs_dense"] = legs["dense"]["kernel_us"] / legs[name]["kernel_us"]
+            legs[name]["speedup_vs_dense"] = legs["dense"]["us_per_step"] / legs[name]["us_per_step"]
+            legs[name]["kernel_speedup_vs_dense"] = legs["dense"]["kernel_us"] / legs[name]["kernel_us"]
     res = {"metric": "Double Sparsity decode attention sequences/s (one layer) & achieved HBM GB/s",
            "value": head["sequences_per_s"], "unit": "sequences/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": head["us_per_step"] * 1e-3, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
            "config": {"workload": "llama2_7b_ds_decode_b16_h32_d128_s8192_r8_k512", "batch": B, "heads": H,
                       "head_dim": d, "seq_len": S, "label_channels": 8, "heavy_tokens": 512,
-                      "cache_ring_copies": R, "launch": "graph"},
+                      "cache_ring_copies": R, "launch": "graph",
+                      "timing": "HIP events around the timed graph replays"},
            "roofline": {"bound": "hbm", "achieved": round(head["achieved_GBps"], 1), "peak": PEAK_GBS,
                         "unit": "GB/s", "frac": round(head["achieved_GBps"] / PEAK_GBS, 4),
                         "traffic": traffic_from_profile("ds_decode_kernel", DS_SOURCES, head["k"]),
@@ -693,52 +773,6 @@ def run_ds_decode(args):
            "legs": legs, "device": torch.cuda.get_device_name(0)}
     res["cpu_baseline"] = None if args.no_cpu else ds_cpu_baseline(base, min(args.cpu_seconds, 10.0))
     print(json.dumps(res))
-
-
-def _replay_timed(torch, f, steps, warmup, G=60):
-    """Warm up, then time exactly `steps` calls of f(i, stream) replayed from
-    HIP graphs of G calls; returns seconds."""
-    cache = {}
-
-    def graph_of(count):
-        if count not in cache:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                s = torch.cuda.current_stream()
-                for i in range(count):
-                    f(i, s)
-            cache[count] = g
-        return cache[count]
-    full, tail = divmod(steps, G)
-    wfull, wtail = divmod(warmup, G)
-    plan_warm = [G] * wfull + ([wtail] if wtail else [])
-    plan_timed = [G] * full + ([tail] if tail else [])
-    for cnt in set(plan_warm + plan_timed):
-        graph_of(cnt)
-    for cnt in plan_warm:
-        cache[cnt].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for cnt in plan_timed:
-        cache[cnt].replay()
-    torch.cuda.synchronize()
-    return time.perf_counter() - t0
-
-
-def _graph_us(torch, fn, count=240):
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        s = torch.cuda.current_stream()
-        for i in range(count):
-            fn(i, s)
-    g.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) * 1e3 / count
 
 
 def counters_run():
@@ -774,28 +808,21 @@ def counters_run():
     print(json.dumps({"counters_run": "done", "forwards": 60, "K": K, "copy_bytes": 256 << 20}))
 
 
-def cpu_baseline(wl, Wh, K, seconds):
-    """The oracle as it stands, per token, on the host: bounded by `seconds`."""
-    import numpy as np
-    import oracle
+# ---------------------------------------------------------------------------
+# CPU baselines: the oracle as it stands, timed on the host
+# ---------------------------------------------------------------------------
+def host_cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo) and the CPUs visible."""
+    name = None
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
-    c = oracle.column_norms(Wh)  # init-time, not timed (the library precomputes c too)
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        x = wl.token(2, 0, done)
-        oracle.forward(Wh, c, x, "topk", K=K)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or done >= 256:
-            break
-    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} tokens of the 4096x11008 bf16 layer at K={K} (fp64 numpy oracle: scores, "
-                      f"lexsort top-K, gathered product), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    name = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": name, "cpus_visible": os.cpu_count()}
 
 
 def _oracle_threads():
@@ -804,6 +831,49 @@ def _oracle_threads():
         return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         return 1
+
+
+def _timed_oracle(run_one, seconds, max_units):
+    """Calls run_one(i) until `seconds` pass or max_units are done; returns
+    (units, elapsed seconds)."""
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        run_one(done)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or done >= max_units:
+            return done, el
+
+
+def _two_thread_settings(run_one, seconds, max_units, unit, describe):
+    """The oracle at one BLAS/OpenMP thread and at the library's default
+    thread count (all cores); the all-thread run is the reported value."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl is installed here
+        threadpool_limits = None
+    half = seconds / 2
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            d1, e1 = _timed_oracle(run_one, half, max_units)
+        single = {"value": round(d1 / e1, 4), "unit": unit, "cores": 1,
+                  "sample": f"{d1} {describe}, {e1:.1f} s"}
+    dn, en = _timed_oracle(run_one, half, max_units)
+    return {"value": round(dn / en, 4), "unit": unit, "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"{dn} {describe}, {en:.1f} s", "single_thread": single, "host": host_cpu_model()}
+
+
+def cpu_baseline(wl, Wh, K, seconds):
+    """The oracle as it stands, per token, on the host (scores, lexsort top-K,
+    gathered fp64 product), bounded by `seconds`."""
+    import oracle
+    c = oracle.column_norms(Wh)  # init-time, not timed (the library precomputes c too)
+    return _two_thread_settings(lambda i: oracle.forward(Wh, c, wl.token(2, 0, i % NTOK), "topk", K=K),
+                                seconds, NTOK, "tokens/s",
+                                f"tokens of the 4096x11008 bf16 layer at K={K} (fp64 numpy oracle: scores, "
+                                "lexsort top-K, gathered product)")
 
 
 def workload_cpu_baseline(leg, host_w, seconds):
@@ -815,74 +885,56 @@ def workload_cpu_baseline(leg, host_w, seconds):
     import workloads as wl
     name, B, lins = leg[:3]
     cs = {(cfg, li): oracle.column_norms(host_w[(cfg, li)]) for cfg, li, _ in lins}
-    done = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one(i):
         for cfg, li, gk in lins:
-            x = wl.token(cfg, li, done)
-            mode = gk["gate"]
-            oracle.forward(host_w[(cfg, li)], cs[(cfg, li)], x, mode, K=gk.get("K"), s_keep=gk.get("s_keep"))
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or done >= 64:
-            break
-    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
-            "sample": f"{done} tokens through the {len(lins)} linears of leg {name} (fp64 numpy oracle per "
-                      f"linear: scores, select, gathered product), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+            x = wl.token(cfg, li, i)
+            oracle.forward(host_w[(cfg, li)], cs[(cfg, li)], x, gk["gate"], K=gk.get("K"), s_keep=gk.get("s_keep"))
+    return _two_thread_settings(one, seconds, 64, "tokens/s",
+                                f"tokens through the {len(lins)} linears of leg {name} (fp64 numpy oracle per "
+                                "linear: scores, select, gathered product)")
 
 
 def ffn_cpu_baseline(host, Ks, tokens, seconds):
-    """The sparse-linear oracle through the FFN chain on the host, per token:
-    gate and up forwards, h = bf16(SiLU(g) u), down forward; bounded by
-    `seconds` (column norms precomputed, as the library does at init)."""
-    import numpy as np
+    """The FFN-chain oracle (oracle.ffn_chain: gate and up forwards, h =
+    bf16(SiLU(g) u) rounded once, down forward) on the host, per token,
+    bounded by `seconds` (column norms precomputed, as the library does at
+    init)."""
     import oracle
-    import workloads as wl
     cs = [oracle.column_norms(W) for W in host]
-    done = 0
-    t0 = time.perf_counter()
-    while True:
-        x = tokens[done % len(tokens)]
-        g = oracle.forward(host[0], cs[0], x, "topk", K=Ks[0])["y"]
-        u = oracle.forward(host[1], cs[1], x, "topk", K=Ks[1])["y"]
-        h = wl.f32_to_bf16_bits((g / (1.0 + np.exp(-g)) * u).astype(np.float32))
-        oracle.forward(host[2], cs[2], h, "topk", K=Ks[2])
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or done >= 64:
-            break
-    return {"value": round(done / el, 4), "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
-            "sample": f"{done} tokens through gate/up 11008x4096 and down 4096x11008 at K={Ks} (fp64 numpy "
-                      f"oracle per projection, numpy SiLU(g) u), {el:.1f} s on {os.cpu_count()} host CPUs visible"}
+    kw = [dict(mode="topk", K=K) for K in Ks]
+    return _two_thread_settings(
+        lambda i: oracle.ffn_chain(host[0], cs[0], kw[0], host[1], cs[1], kw[1], host[2], cs[2], kw[2],
+                                   tokens[i % len(tokens)]),
+        seconds, 64, "tokens/s",
+        f"tokens through gate/up 11008x4096 and down 4096x11008 at K={Ks} (fp64 numpy oracle.ffn_chain)")
 
 
 def ds_cpu_baseline(case, seconds):
     """The Double Sparsity oracle on the host, one (sequence, head) pair at a
     time (label cache, fp32 label scores, lexsort top-k, fp64 attention),
     bounded by `seconds`; reported per sequence (32 heads)."""
-    import numpy as np
     from oracle import double_sparse as ods
     from workloads import decode_attention as wda
     inp = wda.make_inputs(case, batch=1)
     S, k = case.max_seq, case.k
-    done = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def one(done):
         h = done % case.heads
         lab = ods.label_cache(inp.key[:, h:h + 1], inp.channels[h:h + 1])[0, 0]
         s = ods.approx_scores(inp.q[0, h], lab, inp.channels[h], S)
         idx = ods.heavy_tokens(s, k)
         ods.sparse_attention(inp.q[0, h], inp.key[0, h], inp.value[0, h], idx, case.head_dim ** -0.5)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or done >= case.batch * case.heads:
-            break
-    return {"value": round(done / case.heads / el, 4), "unit": "sequences/s", "cores": _oracle_threads(),
-            "kind": "oracle",
-            "sample": f"{done} (sequence, head) pairs (the heads of one {S}-token sequence, repeated: as many "
-                      f"pairs as one batch-{case.batch} step) at r={case.r}, k={k} (numpy oracle: label cache, "
-                      f"fp32 label scores, lexsort top-k, fp64 attention), {el:.1f} s on {os.cpu_count()} host "
-                      f"CPUs visible; sequences/s = pairs/s / {case.heads} heads"}
+    res = _two_thread_settings(one, seconds, case.batch * case.heads, "pairs/s",
+                               f"(sequence, head) pairs at r={case.r}, k={k} (numpy oracle: label cache, fp32 label "
+                               "scores, lexsort top-k, fp64 attention)")
+    # reported per sequence: pairs/s / heads
+    for d in (res, res.get("single_thread")):
+        if d:
+            d["value"] = round(d["value"] / case.heads, 4)
+            d["unit"] = "sequences/s"
+    res["sample"] += f"; sequences/s = pairs/s / {case.heads} heads"
+    return res
 
 
 if __name__ == "__main__":

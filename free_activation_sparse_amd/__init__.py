@@ -34,7 +34,7 @@ EXPORTED = [
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
     "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
-    "ds_label_cache_update", "ds_decode_attention",
+    "sparse_linear_gather_ceiling", "ds_label_cache_update", "ds_decode_attention",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_set_fused.restype = ctypes.c_int
     L.sparse_linear_sync_status.argtypes = [_vp, _vp]
     L.sparse_linear_sync_status.restype = ctypes.c_int
+    L.sparse_linear_gather_ceiling.argtypes = [_vp, _vp, _i32, _vp, _vp]
+    L.sparse_linear_gather_ceiling.restype = ctypes.c_int
     L.ds_label_cache_update.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     L.ds_label_cache_update.restype = ctypes.c_int
     L.ds_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -187,6 +189,11 @@ def sparse_linear_forward_stages(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype
     _check(lib().sparse_linear_forward_stages(h, x_ptr, B, y_ptr, y_dtype, mask_ptr or None, count_ptr or None,
                                               thresh_ptr or None, stages, stream or None),
            "sparse_linear_forward_stages")
+
+
+def sparse_linear_gather_ceiling(h: int, idx_ptr: int, count: int, sink_ptr: int, stream: int = 0) -> None:
+    _check(lib().sparse_linear_gather_ceiling(h, idx_ptr, count, sink_ptr, stream or None),
+           "sparse_linear_gather_ceiling")
 
 
 def sparse_linear_set_deterministic(h: int, on: bool) -> None:

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_linear.so")
-SOURCES = ["api.cpp", "layout.hip", "gate.hip", "product.hip", "fused.hip", "union_product.hip", "ffn.hip", "double_sparse.hip"]
+SOURCES = ["api.cpp", "layout.hip", "gate.hip", "product.hip", "fused.hip", "union_product.hip", "ffn.hip", "double_sparse.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 

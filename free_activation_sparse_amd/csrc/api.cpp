@@ -168,6 +168,19 @@ bool union_spec(const sl_linear* h, int B, bool dense) {
   return 1.0 - std::pow(1.0 - f, (double)B) >= 0.98;
 }
 
+// Reports (and clears) a timed-out hand-off that an earlier fused forward of
+// this handle recorded in its host-visible error word. Needs no
+// synchronization: the kernel stores the word with system scope, so a
+// forward that has completed is seen by the next call at the latest.
+sl_status take_async_error(const sl_linear* h) {
+  if (h->herr == nullptr) return SL_OK;
+  const uint32_t e = __atomic_exchange_n(h->herr, 0u, __ATOMIC_ACQ_REL);
+  if (e == 0) return SL_OK;
+  return fail(SL_ERR_HIP,
+              "fused forward: a %s wait timed out in an earlier call on this handle (that call's y is incomplete)",
+              e == 1 ? "product workgroup's gate" : "gate workgroup's acknowledgement");
+}
+
 sl_status check_device(const sl_linear* h) {
   int dev = -1;
   SL_HIP(hipGetDevice(&dev));
@@ -185,6 +198,7 @@ void free_handle(sl_linear* h) {
   (void)hipFree(h->upartials);
   (void)hipFree(h->uctr);
   (void)hipFree(h->fsync);
+  if (h->herr) (void)hipHostFree(h->herr);
   delete h;
 }
 
@@ -279,6 +293,11 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
     if ((e = hipMalloc(&h->fsync, sizeof(sl::FusedSync))) != hipSuccess) return cleanup_fail(e, "hipMalloc(sync)");
     if ((e = hipMemsetAsync(h->fsync, 0, sizeof(sl::FusedSync), s)) != hipSuccess)
       return cleanup_fail(e, "hipMemsetAsync(sync)");
+    if ((e = hipHostMalloc((void**)&h->herr, 64, hipHostMallocMapped | hipHostMallocCoherent)) != hipSuccess)
+      return cleanup_fail(e, "hipHostMalloc(error word)");
+    *h->herr = 0u;
+    if ((e = hipHostGetDevicePointer((void**)&h->herr_dev, h->herr, 0)) != hipSuccess)
+      return cleanup_fail(e, "hipHostGetDevicePointer(error word)");
     if ((e = hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
       return cleanup_fail(e, "hipDeviceGetAttribute(compute units)");
 
@@ -344,6 +363,7 @@ static sl_status forward_impl(sl_handle h, const void* x, int32_t B, void* y, sl
   if (stages < 1 || stages > 3) return fail(SL_ERR_ARG, "stages=%d outside 1..3", stages);
   sl_status st = check_device(h);
   if (st != SL_OK) return st;
+  if ((st = take_async_error(h)) != SL_OK) return st;
   hipStream_t s = (hipStream_t)stream;
   const bool full = (stages & SL_STAGE_GATE) && (stages & SL_STAGE_PRODUCT);
   const bool gate_wanted = !dense && (stages & SL_STAGE_GATE) &&
@@ -421,6 +441,15 @@ sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, c
       sl_status st = check_device(h);
       if (st != SL_OK) return st;
     }
+    // one handle twice would make two linears of the launch share its
+    // hand-off state and scratch
+    for (int a = 0; a < count; ++a)
+      for (int b = a + 1; b < count; ++b)
+        if (handles[a] == handles[b]) return fail(SL_ERR_ARG, "linears %d and %d are the same handle", a, b);
+    for (int l = 0; l < count; ++l) {
+      sl_status st = take_async_error(handles[l]);
+      if (st != SL_OK) return st;
+    }
     bool grouped = count > 1 && y_dtype == SL_F32;
     for (int l = 0; l < count && grouped; ++l) {
       const sl_linear* h = handles[l];
@@ -460,6 +489,8 @@ sl_status sparse_linear_forward_ffn(sl_handle gate, sl_handle up, sl_handle down
   try {
     g_last_error.clear();
     if (gate == nullptr || up == nullptr || down == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+    if (gate == up || gate == down || up == down)
+      return fail(SL_ERR_ARG, "gate, up and down must be three different handles");
     if (x == nullptr || y == nullptr || workspace == nullptr) return fail(SL_ERR_ARG, "NULL pointer");
     if (gate->m != up->m || gate->n != up->n || down->n != up->m)
       return fail(SL_ERR_ARG, "shapes: gate %lldx%lld, up %lldx%lld, down %lldx%lld do not chain", (long long)gate->m,
@@ -537,15 +568,24 @@ sl_status sparse_linear_sync_status(sl_handle h, void* stream) {
   if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
   sl_status st = check_device(h);
   if (st != SL_OK) return st;
-  hipStream_t s = (hipStream_t)stream;
-  SL_HIP(hipStreamSynchronize(s));
-  uint32_t err = 0;
-  SL_HIP(hipMemcpy(&err, &h->fsync->err, sizeof(err), hipMemcpyDeviceToHost));
-  if (err == 0) return SL_OK;
-  const uint32_t zero = 0;
-  SL_HIP(hipMemcpy(&h->fsync->err, &zero, sizeof(zero), hipMemcpyHostToDevice));
-  return fail(SL_ERR_HIP, "fused forward: a %s wait timed out (results of that forward are incomplete)",
-              err == 1 ? "product workgroup's gate" : "gate workgroup's acknowledgement");
+  SL_HIP(hipStreamSynchronize((hipStream_t)stream));
+  return take_async_error(h);
+}
+
+
+sl_status sparse_linear_gather_ceiling(sl_handle h, const int32_t* idx, int32_t count, float* sink, void* stream) {
+  try {
+    g_last_error.clear();
+    if (h == nullptr || idx == nullptr || sink == nullptr) return fail(SL_ERR_ARG, "NULL argument");
+    if (count < 0 || count > h->n) return fail(SL_ERR_ARG, "count=%d outside [0, n=%lld]", (int)count, (long long)h->n);
+    sl_status st = check_device(h);
+    if (st != SL_OK) return st;
+    if (count == 0) return SL_OK;
+    SL_HIP(sl::launch_gather_ceiling(h, idx, count, sink, (hipStream_t)stream));
+    return SL_OK;
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in gather_ceiling");
+  }
 }
 
 sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on) {

@@ -19,7 +19,8 @@
 // product's chunk loads with the gate. Progress: workgroups are dispatched in
 // index order on each XCD, so workgroup 0 holds a CU before any product
 // workgroup exists; every spin is bounded, and a timeout is recorded in the
-// error word (read by sparse_linear_sync_status) instead of hanging.
+// handle's host-visible error word (reported by the handle's next call or by
+// sparse_linear_sync_status) instead of hanging.
 #include "gate_body.h"
 #include "product_body.h"
 
@@ -80,6 +81,7 @@ struct FusedArgs {
   float* partials;
   uint32_t* ctr;
   sl::FusedSync* sync;
+  uint32_t* err;  // host-visible record of a timed-out wait (system scope)
   int use_parts;
   YT* y;
 };
@@ -123,15 +125,14 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
       const int slot = t < sl::kAckSlots ? t : 0;
       uint32_t it = 0, total = 0;
       for (;;) {
-        const uint32_t a = t < sl::kAckSlots
-                               ? __hip_atomic_load(&sync->ack[16 * slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                               : 0u;
-        total = wave_sum(a);
+        const uint32_t ak = t < sl::kAckSlots
+                                ? __hip_atomic_load(&sync->ack[16 * slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0u;
+        total = wave_sum(ak);
         if (total >= (uint32_t)nprod || ++it >= kSpinLimit) break;
         __builtin_amdgcn_s_sleep(8);
       }
-      if (t == 0 && total < (uint32_t)nprod)
-        __hip_atomic_store(&sync->err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t == 0 && total < (uint32_t)nprod) __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (t < sl::kAckSlots) __hip_atomic_store(&sync->ack[16 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t == 0) __hip_atomic_store(&sync->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // a new tag for the next launch's moment parts: anything written
@@ -311,7 +312,7 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
     }
   }
   if (t == 0) {
-    if (pv == 0ull) __hip_atomic_store(&sync->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (pv == 0ull) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   sl::proddev::reduce_out<WT, YT, LPC, FT, ATOMIC>(acc, m, tile, split, splits, sm.p.red, partials, ctr,
@@ -394,7 +395,8 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
   // once (the gate would otherwise wait for workgroups not yet dispatched)
   const int use_parts = 1 + (int64_t)p.tiles * p.splits <= (int64_t)std::max(1, h->cus) * per_cu ? 1 : 0;
   const FusedArgs<uint16_t, YT> a{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau, g, mask, cnt,
-                                 th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, use_parts, (YT*)y};
+                                 th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, h->herr_dev, use_parts,
+                                 (YT*)y};
   fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(a, (const uint16_t*)x,
                                                                                           (int)h->n);
   return hipGetLastError();
@@ -484,7 +486,7 @@ hipError_t go_group(const sl_linear* const* hs, int count, const void* x, float*
     gr.begin[l] = (int)total;
     gr.lin[l] = FusedArgs<uint16_t, float>{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau,
                                            h->gout, nullptr, nullptr, nullptr, (int)tiles[l], (int)splits, chunk,
-                                           h->partials, h->ctr, h->fsync, 0, ys[l]};
+                                           h->partials, h->ctr, h->fsync, h->herr_dev, 0, ys[l]};
     total += tiles[l] * splits;
   }
   gr.begin[count] = (int)total;

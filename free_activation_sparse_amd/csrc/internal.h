@@ -74,8 +74,7 @@ struct MomentPart {
 constexpr int kMaxMomentParts = 32768 / 64;  // the fused forward takes n <= 32768
 struct FusedSync {
   uint64_t flag;  // 0, or the kept-set pair: kthr | (jlast + 2) << 32
-  uint32_t err;   // nonzero after a timed-out wait (1: product side, 2: gate side)
-  uint32_t pad[13];
+  uint32_t pad[14];
   uint32_t ack[kAckSlots * 16];  // slot i at ack[16 * i]: product workgroups pw = i mod kAckSlots
   uint32_t gen;                  // launches completed (mod 2^32), advanced by the gate workgroup at its end
   uint32_t pad2[15];
@@ -107,6 +106,12 @@ struct sl_linear {
   int64_t upart_len = 0;
   uint32_t* uctr = nullptr;     // [utiles]
   sl::FusedSync* fsync = nullptr;  // fused gate + product hand-off
+  // Timed-out hand-off record of the fused forward: pinned, mapped host memory
+  // that the kernels write (system scope) and the host reads without a
+  // synchronization; 1 = a product workgroup's wait for the gate, 2 = the gate
+  // workgroup's wait for the product workgroups.
+  uint32_t* herr = nullptr;        // host address
+  uint32_t* herr_dev = nullptr;    // the same word as the device sees it
   int cus = 0;                     // compute units of the device
 
   int plan_rows = 0, plan_splits = 0;  // overrides (0 = automatic)
@@ -154,6 +159,8 @@ struct DsDecodeParams {
 hipError_t launch_ds_decode(const DsDecodeParams& p, int batch, int head_dim, int r, hipStream_t s);
 hipError_t launch_ds_label(const uint16_t* key, uint16_t* label, const int32_t* channels, const int32_t* start,
                            int batch, int heads, int max_seq, int head_dim, int r, int span, hipStream_t s);
+// Read-only gather of the columns idx[0 .. count) (bandwidth ceiling probe).
+hipError_t launch_gather_ceiling(const sl_linear* h, const int32_t* idx, int count, float* sink, hipStream_t s);
 // Union-product workgroups resident per compute unit (occupancy query).
 int union_workgroups_per_cu(int rows, sl_dtype ydt, bool atomic);
 hipError_t launch_union_product(const sl_linear* h, const UnionPlan& p, const void* x, int B,

@@ -116,6 +116,15 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
  * Asynchronous on `stream`; the caller keeps x, y and the optional outputs
  * alive until the stream has completed. A handle's scratch is shared by its
  * calls, so one handle must not run on two streams at once.
+ *
+ * Failed hand-off: the fused launch's workgroups wait for each other with
+ * bounded spins. A wait that gives up (about a second; in-order workgroup
+ * dispatch rules it out on a working device) leaves that forward's y
+ * incomplete and is recorded in a host-visible word of the handle, without
+ * any synchronization. The handle's next forward (any of the forward entry
+ * points) then returns SL_ERR_HIP before enqueuing anything, and
+ * sparse_linear_sync_status reports it at once. Callers that must know that a
+ * particular forward completed call sparse_linear_sync_status after it.
  */
 sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, sl_dtype y_dtype,
                                 uint8_t* mask_out, int32_t* count_out, double* thresh_out,
@@ -141,10 +150,11 @@ sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, 
  * gates share their mode, y_dtype is fp32, n % 4 == 0 and x is 8-byte
  * aligned; otherwise the linears run one after another. No mask, count or
  * threshold outputs. Errors: NULL arrays or pointers, count outside 1..8,
- * differing n or dtypes, a handle on another device (SL_ERR_ARG); nothing is
- * launched then. Asynchronous on `stream`; the handles' scratch is in use
- * until it completes. Timed-out hand-offs are reported per handle by
- * sparse_linear_sync_status.
+ * differing n or dtypes, the same handle twice, a handle on another device
+ * (SL_ERR_ARG); a recorded failed hand-off of any of the handles
+ * (SL_ERR_HIP, see sparse_linear_forward); nothing is launched then.
+ * Asynchronous on `stream`; the handles' scratch is in use until it
+ * completes.
  */
 sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, const void* x, void* const* ys,
                                       sl_dtype y_dtype, void* stream);
@@ -167,8 +177,9 @@ sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, c
  *              sparse_linear_ffn_workspace_bytes(up) bytes: g and u (fp32 [m])
  *              and h (bf16 [m]) are left there after the call.
  *
- * Errors: NULL arguments, shapes that do not chain, a short or misaligned
- * workspace (SL_ERR_ARG); weights other than bf16 (SL_ERR_UNSUPPORTED).
+ * Errors: NULL arguments, gate, up and down not three different handles,
+ * shapes that do not chain, a short or misaligned workspace (SL_ERR_ARG);
+ * weights other than bf16 (SL_ERR_UNSUPPORTED).
  * Asynchronous on `stream`; the workspace is in use until it completes.
  */
 int64_t sparse_linear_ffn_workspace_bytes(sl_handle up);
@@ -220,6 +231,19 @@ sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, vo
                                        int32_t stages, void* stream);
 
 /*
+ * sparse_linear_gather_ceiling -- measurement only: read the handle's weight
+ * columns idx[0 .. count) (device int32, each clamped into [0, n)) once, with
+ * no gate, no product and no output beyond a checksum that is never stored in
+ * practice (sink: device fp32[1], written only if the checksum hits a fixed
+ * value). Its duration is the practical bandwidth ceiling of gathering the
+ * same weight bytes that a forward with that kept set reads (Spark
+ * Transformer article, section 3.1: only the active inputs' weight vectors
+ * are read). count in [0, n], else SL_ERR_ARG; count == 0 launches nothing.
+ * Asynchronous on `stream`.
+ */
+sl_status sparse_linear_gather_ceiling(sl_handle h, const int32_t* idx, int32_t count, float* sink, void* stream);
+
+/*
  * Split reduction mode. The product kernel splits the kept inputs into chunks
  * whose partial sums are added per output row. By default (on == 0) fp32
  * outputs take fp32 atomic adds, which is fastest but lets the summation order
@@ -237,11 +261,12 @@ sl_status sparse_linear_set_fused(sl_handle h, int32_t on);
 
 /*
  * Synchronize `stream` and report whether any fused forward of this handle
- * since the last call had a hand-off wait time out (its gate workgroup not
+ * since the last report had a hand-off wait time out (its gate workgroup not
  * running within about a second, which in-order workgroup dispatch rules out
  * on an otherwise working device). Returns SL_OK, or SL_ERR_HIP with
  * sparse_linear_last_error describing the wait; the record is then cleared.
- * Such a forward's y is incomplete.
+ * Such a forward's y is incomplete. Without this call the record is reported
+ * by the handle's next forward (see sparse_linear_forward).
  */
 sl_status sparse_linear_sync_status(sl_handle h, void* stream);
 

@@ -14,6 +14,17 @@ def to_dev(a, torch, device="cuda:0"):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
 
 
+def tile_rows(m, seed, block=128):
+    """Sampled output rows that cover every row tile of the kernels' launch
+    shapes: one random row from each block of `block` rows (the kernels use
+    128-, 256- and 512-row tiles, so every tile of any of them gets at least
+    one), plus the last row."""
+    g = np.random.default_rng(seed)
+    rows = [int(g.integers(b, min(m, b + block))) for b in range(0, m, block)]
+    rows.append(m - 1)
+    return np.unique(np.asarray(rows, dtype=np.int64))
+
+
 def gate_kwargs(mode, K=None, s_keep=None, tau=None):
     if mode == "topk":
         return dict(gate="topk", K=K)

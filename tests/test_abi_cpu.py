@@ -107,6 +107,7 @@ def test_forward_rejects_null_handle_and_pointers(slib):
     assert L.sparse_linear_set_deterministic(None, 1) == 1
     assert L.sparse_linear_set_fused(None, 1) == 1
     assert L.sparse_linear_sync_status(None, None) == 1
+    assert L.sparse_linear_gather_ceiling(None, 1, 1, 1, None) == 1
 
 
 def test_forward_ffn_rejects_bad_arguments(slib):

@@ -35,3 +35,25 @@ def test_algorithmic_bytes():
         B * H * (S * r * 2 + k * d * 4 + d * 2 + d * 4) + H * r * 4 + B * 4
     # dense (k >= n): no label rows
     assert bench.ds_algorithmic_bytes(B, H, S, d, r, S) == B * H * (S * d * 4 + d * 6) + H * r * 4 + B * 4
+
+
+def test_cpu_baseline_reports_both_thread_settings():
+    sys.path.insert(0, ROOT)
+    import bench
+    calls = []
+    res = bench._two_thread_settings(lambda i: calls.append(i), 0.05, 50, "tokens/s", "units of a test")
+    for k in ("value", "unit", "cores", "kind", "sample"):
+        assert k in res
+    assert res["kind"] == "oracle" and res["unit"] == "tokens/s" and res["value"] > 0
+    assert res["single_thread"]["cores"] == 1 and res["single_thread"]["value"] > 0
+    assert res["host"]["cpus_visible"] == os.cpu_count()
+    assert len(calls) <= 100
+
+
+def test_parse_defaults_and_legs():
+    sys.path.insert(0, ROOT)
+    import bench
+    a = bench.parse([])
+    assert a.gpus == 1 and a.workload == "llama7b_down" and a.only == "all"
+    for leg in ("sparse50", "sparse65", "fixed50", "dense", "ceiling"):
+        assert bench.parse(["--only", leg]).only == leg

@@ -144,3 +144,33 @@ def test_group_graph_replays(fas):
     for pair in pairs:
         for l in pair:
             l.close()
+
+
+def test_group_and_ffn_reject_duplicate_handles(fas):
+    # one handle twice would share its hand-off state and scratch between two
+    # linears of one launch: rejected before anything is enqueued
+    n, m = 512, 1024
+    Ws = [wl.random_matrix(240 + i, *s, "bf16") for i, s in enumerate(((m, n), (m, n), (n, m)))]
+    cs = [oracle.column_norms(W) for W in Ws]
+    ls = [_layer(fas, W, c, "topk", K=k) for W, c, k in zip(Ws, cs, (300, 300, 500))]
+    x = to_dev(wl.random_tokens(241, 1, n, "bf16")[0], torch)
+    ys = [torch.full((m,), 7.0, device="cuda:0") for _ in range(2)]
+    torch.cuda.synchronize()
+    with pytest.raises(fas.SparseLinearError) as e:
+        fas.SparseLinear.forward_group([ls[0], ls[0]], x, ys)
+    assert e.value.status == fas.SL_ERR_ARG and "same handle" in str(e.value)
+    with pytest.raises(fas.SparseLinearError) as e:
+        fas.SparseLinear.forward_group([ls[0], ls[1], ls[0]], x, ys + [torch.empty(m, device="cuda:0")])
+    assert e.value.status == fas.SL_ERR_ARG
+    torch.cuda.synchronize()
+    assert bool((ys[0] == 7.0).all()) and bool((ys[1] == 7.0).all())  # nothing ran
+    for args in ((ls[0], ls[0], ls[2]), (ls[0], ls[1], ls[0]), (ls[1], ls[1], ls[1])):
+        with pytest.raises(fas.SparseLinearError) as e:
+            fas.SparseLinear.forward_ffn(*args, x)
+        assert e.value.status == fas.SL_ERR_ARG
+    # distinct handles still run
+    ys = fas.SparseLinear.forward_group([ls[0], ls[1]], x)
+    for l in ls:
+        l.sync_status()
+    for l in ls:
+        l.close()

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity_util import REL_L2_TOL, check_token, gate_kwargs, rel_l2, to_dev
+from parity_util import REL_L2_TOL, check_token, gate_kwargs, rel_l2, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -74,11 +74,11 @@ def test_llama7b_down_full_size(fas, llama_down, sparsity, fused):
     K = wl.k_from_sparsity(W.shape[1], sparsity)
     layer = _layer(fas, W, c, "topk", K=K)
     layer.set_fused(fused)
-    rows = np.random.default_rng(7).choice(W.shape[0], 96, replace=False)
+    rows = tile_rows(W.shape[0], 7)
     for t in range(12):
         x = wl.token(2, 0, t)
         print(f"[llama-down p={sparsity}] token {t}", flush=True)
-        full = t < 2  # the whole y for two tokens, sampled rows for the rest
+        full = t < 2  # the whole y for two tokens, a row of every tile for the rest
         check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=None if full else rows, ctx="llama-down")
     layer.close()
 
@@ -99,16 +99,17 @@ def test_llama7b_down_plans(fas, llama_down):
 
 
 # ---------------------------------------------------------------- STAT gate (config 4 shapes)
-@pytest.mark.parametrize("linear", [0, 2])
+@pytest.mark.parametrize("linear", [0, 1, 2])
 def test_phi4_stat_gate_full_size(fas, linear):
     W = wl.weight(4, linear)
     c = oracle.column_norms(W)
     layer = _layer(fas, W, c, "stat", s_keep=0.10)
-    rows = np.random.default_rng(9).choice(W.shape[0], 64, replace=False)
+    rows = tile_rows(W.shape[0], 9 + linear)
     for t in range(8):
         x = wl.token(4, linear, t)
         print(f"[phi4 stat linear {linear}] token {t}", flush=True)
-        check_token(_fwd(layer, x), 0, W, c, x, "stat", s_keep=0.10, rows=rows, ctx="phi4-stat")
+        check_token(_fwd(layer, x), 0, W, c, x, "stat", s_keep=0.10, rows=None if t == 0 else rows,
+                    ctx="phi4-stat")
     layer.close()
 
 
@@ -120,11 +121,12 @@ def test_llama3_block_linears(fas):
         c = oracle.column_norms(W)
         K = wl.k_from_sparsity(lin.n, round(ps[li], 6))
         layer = _layer(fas, W, c, "topk", K=K)
-        rows = np.random.default_rng(li).choice(lin.m, 48, replace=False)
+        rows = tile_rows(lin.m, li)
         for t in range(3):
             x = wl.token(3, li, t)
             print(f"[llama3 {lin.name}] token {t} K={K}", flush=True)
-            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=rows, ctx=f"llama3-{lin.name}")
+            check_token(_fwd(layer, x), 0, W, c, x, "topk", K=K, rows=None if t == 0 else rows,
+                        ctx=f"llama3-{lin.name}")
         layer.close()
         del W
 

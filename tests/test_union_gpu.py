@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity_util import REL_L2_TOL, check_token, gate_kwargs, rel_l2, to_dev
+from parity_util import REL_L2_TOL, check_token, gate_kwargs, rel_l2, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -32,39 +32,44 @@ def _fwd(layer, X, **kw):
     return out
 
 
-def _check_all(out, W, c, X, mode, rows=None, ctx="", **g):
+def _check_all(out, W, c, X, mode, rows=None, ctx="", full=(), **g):
+    """Every token of the batch; tokens listed in `full` compare their whole y."""
     for b in range(X.shape[0]):
-        check_token(out, b, W, c, X[b], mode, rows=rows, ctx=f"{ctx} b={b}", **g)
+        check_token(out, b, W, c, X[b], mode, rows=None if b in full else rows, ctx=f"{ctx} b={b}", **g)
 
 
 # ---------------------------------------------------------------- config 4: Phi-4 FFN, STAT gate
-@pytest.mark.parametrize("linear", [0, 2])
+@pytest.mark.parametrize("linear", [0, 1, 2])
 def test_phi4_stat_batched(fas, linear):
     W = wl.weight(4, linear)
     c = oracle.column_norms(W)
     layer = _layer(fas, W, c, "stat", 8, s_keep=0.10)
-    rows = np.random.default_rng(linear).choice(W.shape[0], 48, replace=False)
+    rows = tile_rows(W.shape[0], linear)
     first = 0
     for B in (2, 4, 8):
         X = wl.tokens(4, linear, first, B)
         first += B
         print(f"[phi4 stat linear {linear}] B={B}", flush=True)
-        _check_all(_fwd(layer, X), W, c, X, "stat", rows=rows, ctx=f"phi4 B={B}", s_keep=0.10)
+        _check_all(_fwd(layer, X), W, c, X, "stat", rows=rows, ctx=f"phi4 B={B}", full=(0,) if B == 8 else (),
+                   s_keep=0.10)
     layer.close()
 
 
 # ---------------------------------------------------------------- config 5: Qwen2.5-7B FFN, B = 16
-@pytest.mark.parametrize("linear", [0, 2])
+@pytest.mark.parametrize("linear", [0, 1, 2])
 @pytest.mark.parametrize("sparsity", [0.65, 0.90])
 def test_qwen_b16_topk(fas, linear, sparsity):
     W = wl.weight(5, linear)
     c = oracle.column_norms(W)
     K = wl.k_from_sparsity(W.shape[1], sparsity)
     layer = _layer(fas, W, c, "topk", 16, K=K)
-    rows = np.random.default_rng(linear + 7).choice(W.shape[0], 40, replace=False)
-    X = wl.tokens(5, linear, 0, 16)
-    print(f"[qwen linear {linear} p={sparsity}] K={K}", flush=True)
-    _check_all(_fwd(layer, X), W, c, X, "topk", rows=rows, ctx=f"qwen p={sparsity}", K=K)
+    rows = tile_rows(W.shape[0], linear + 7)
+    # two batches of the 16 x 16 tokens: the first and the tenth
+    for batch in (0, 9):
+        X = wl.tokens(5, linear, 16 * batch, 16)
+        print(f"[qwen linear {linear} p={sparsity}] K={K} batch {batch}", flush=True)
+        _check_all(_fwd(layer, X), W, c, X, "topk", rows=rows, ctx=f"qwen p={sparsity} batch {batch}",
+                   full=(0,) if batch == 0 else (), K=K)
     layer.close()
 
 
