@@ -34,6 +34,7 @@ EXPORTED = [
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
     "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
+    "sparse_linear_forward_ffn_noalloc",
     "sparse_linear_gather_ceiling", "ds_label_cache_update", "ds_decode_attention",
 ]
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_ffn_workspace_bytes.restype = _i64
     L.sparse_linear_forward_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _vp]
     L.sparse_linear_forward_ffn.restype = ctypes.c_int
+    L.sparse_linear_forward_ffn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp]
+    L.sparse_linear_forward_ffn_noalloc.restype = ctypes.c_int
     L.sparse_linear_get_norms.argtypes = [_vp, _vp, _vp]
     L.sparse_linear_get_norms.restype = ctypes.c_int
     L.sparse_linear_destroy.argtypes = [_vp]
@@ -142,6 +145,12 @@ def sparse_linear_forward_ffn(gate: int, up: int, down: int, x_ptr: int, y_ptr: 
                               ws_bytes: int, stream: int = 0) -> None:
     _check(lib().sparse_linear_forward_ffn(gate, up, down, x_ptr, y_ptr, y_dtype, ws_ptr, ws_bytes, stream or None),
            "sparse_linear_forward_ffn")
+
+
+def sparse_linear_forward_ffn_noalloc(gate: int, up: int, down: int, x_ptr: int, y_ptr: int, y_dtype: int,
+                                      stream: int = 0) -> None:
+    _check(lib().sparse_linear_forward_ffn_noalloc(gate, up, down, x_ptr, y_ptr, y_dtype, stream or None),
+           "sparse_linear_forward_ffn_noalloc")
 
 
 def ds_label_cache_update(key_ptr: int, label_ptr: int, channels_ptr: int, start_ptr: int, batch: int, heads: int,

@@ -259,6 +259,13 @@ sl_status sparse_linear_init(sl_handle* out, const void* W, sl_dtype w_dtype, sl
     int dev = -1;
     SL_HIP(hipGetDevice(&dev));
     hipStream_t s = (hipStream_t)stream;
+    {
+      // set-up of the allocation-free FFN entry point: the static workspace's
+      // address on this device (cached; a failure here is reported by that
+      // entry point, which looks it up again)
+      void* ws = nullptr;
+      (void)sl::ffn_scratch(dev, &ws);
+    }
 
     sl_linear* h = new (std::nothrow) sl_linear();
     if (!h) return fail(SL_ERR_OOM, "host allocation failed");
@@ -513,6 +520,24 @@ sl_status sparse_linear_forward_ffn(sl_handle gate, sl_handle up, sl_handle down
     return forward_impl(down, hb, 1, y, y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
   } catch (...) {
     return fail(SL_ERR_OOM, "unexpected host exception in forward_ffn");
+  }
+}
+
+sl_status sparse_linear_forward_ffn_noalloc(sl_handle gate, sl_handle up, sl_handle down, const void* x, void* y,
+                                            sl_dtype y_dtype, void* stream) {
+  try {
+    g_last_error.clear();
+    if (gate == nullptr || up == nullptr || down == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
+    if (up->m > sl::kFfnScratchMaxM)
+      return fail(SL_ERR_UNSUPPORTED, "intermediate width m=%lld exceeds the static workspace's %lld",
+                  (long long)up->m, (long long)sl::kFfnScratchMaxM);
+    sl_status st = check_device(up);
+    if (st != SL_OK) return st;
+    void* ws = nullptr;
+    SL_HIP(sl::ffn_scratch(up->device, &ws));
+    return sparse_linear_forward_ffn(gate, up, down, x, y, y_dtype, ws, (int64_t)sl::kFfnScratchBytes, stream);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_ffn_noalloc");
   }
 }
 

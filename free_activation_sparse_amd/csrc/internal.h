@@ -131,6 +131,15 @@ hipError_t launch_gate(const sl_linear* h, const void* x, int B, uint8_t* mask_o
 hipError_t launch_zero(float* y, int64_t count, hipStream_t s);
 hipError_t launch_product(const sl_linear* h, const Plan& p, const void* x, const GateOut* g, bool dense,
                           void* y, sl_dtype ydt, hipStream_t s);
+// Static workspace of the allocation-free FFN chain: intermediate widths up to
+// kFfnScratchMaxM (g, u fp32 and h bf16, each piece 256-byte aligned; the
+// widest FFN of the Llama-2/3, Phi-4 and Qwen2.5 shapes is 18944).
+constexpr int64_t kFfnScratchMaxM = 20480;
+constexpr size_t kFfnScratchBytes = 2 * (4 * kFfnScratchMaxM) + 2 * kFfnScratchMaxM;  // 200 KiB
+static_assert(kFfnScratchMaxM % 128 == 0, "every workspace piece stays 256-byte aligned");
+// Device address of the static FFN workspace on `device`, which must be the
+// current device; looked up once per device (hipGetSymbolAddress) and cached.
+hipError_t ffn_scratch(int device, void** ptr);
 // h = bf16(SiLU(g) * u) over m values (sparse FFN chain epilogue).
 hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t m, hipStream_t s);
 // Grouped fused forward (one token) of count <= 8 linears that share x: all

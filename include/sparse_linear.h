@@ -187,6 +187,27 @@ sl_status sparse_linear_forward_ffn(sl_handle gate, sl_handle up, sl_handle down
                                     sl_dtype y_dtype, void* workspace, int64_t workspace_bytes, void* stream);
 
 /*
+ * sparse_linear_forward_ffn_noalloc -- the sparse FFN chain of
+ * sparse_linear_forward_ffn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). It calls no hipMalloc, hipFree or allocating library routine:
+ * g, u and h live in a static device array of the library (200 KiB, one copy
+ * per GPU, held until the process ends), whose address is looked up once per
+ * device at handle init.
+ *
+ *   gate, up, down, x, y, y_dtype, stream   as for sparse_linear_forward_ffn.
+ *
+ * Limit: the intermediate width (up's m) at most 20480, else
+ * SL_ERR_UNSUPPORTED. Every call on a GPU shares that GPU's array, which keeps
+ * the last call's g, u and h (each call overwrites what it reads; nothing has
+ * to start at zero between calls): calls that overlap on one GPU, on one
+ * stream or several, race and must not be made. Other errors as for
+ * sparse_linear_forward_ffn.
+ */
+sl_status sparse_linear_forward_ffn_noalloc(sl_handle gate, sl_handle up, sl_handle down, const void* x, void* y,
+                                            sl_dtype y_dtype, void* stream);
+
+/*
  * sparse_linear_forward_dense -- y = W x for B tokens with every input kept,
  * run by the same product kernel as the sparse path over the identity index
  * list (the dense baseline the sparse forward is compared against).
