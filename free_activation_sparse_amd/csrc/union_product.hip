@@ -59,12 +59,15 @@ __device__ __forceinline__ i16x4 lds_read_tr(const uint8_t* p) {
 __device__ __forceinline__ i16x4 lds_read_b64(const uint8_t* p) { return *(const i16x4*)p; }
 
 // NB: 16-row MFMA blocks per wavefront (tile of R = 64 * NB rows); D: column
-// steps whose loads are in flight ahead of the one being multiplied.
-template <typename YT, bool ATOMIC, int NB, int D>
+// steps whose loads are in flight ahead of the one being multiplied; SPEC:
+// the first D steps are loaded before the union is known (a compile-time
+// choice: behind a run-time branch the wait for the x loads became a wait
+// for every load in flight, the speculative weights included).
+template <typename YT, bool ATOMIC, int NB, int D, bool SPEC>
 __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ Wt, const uint16_t* __restrict__ x,
                                                    const float* __restrict__ c,
                                                    const sl::GateOut* __restrict__ gout, int m, int n, int B,
-                                                   int tiles, int splits, int chunk, bool dense, bool spec,
+                                                   int tiles, int splits, int chunk, bool dense,
                                                    float* __restrict__ partials, uint32_t* __restrict__ ctr,
                                                    YT* __restrict__ y) {
   constexpr int UR = 64 * NB;          // rows per tile
@@ -95,6 +98,12 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   uint64_t bal[ROUNDS];
   uint16_t xr[ROUNDS][16];
   float cr[ROUNDS];
+  // the B gate pairs: lane b of every wavefront loads token b's pair, first
+  // of all loads (one vector load; as 16 scalar loads the compiler issued
+  // them in three dependent batches), and the pairs are read out per token
+  // below; tokens >= B keep nothing, the dense product keeps everything
+  const uint64_t* gp = (const uint64_t*)gout;  // GateOut: kthr, jlast first
+  const uint64_t gpair = gp[(size_t)((lane & 15) < B ? (lane & 15) : 0) * (sizeof(sl::GateOut) / 8)];
   // all loads unconditional (token and input indices clamped) so they are in
   // flight together, and issued before any weight load (vector loads complete
   // in order); values of tokens >= B are masked out below
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   // union density): the first D steps of a dense prefix, i.e. chunk columns
   // 0 .. 32 D - 1 (clamped into the chunk), go out now; they are kept once
   // the union turns out to start with exactly those columns.
-  if (spec) {
+  if constexpr (SPEC) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
 #pragma unroll
@@ -158,18 +167,17 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
       }
     }
   }
-  // the B gate pairs as scalars (uniform loads, in flight with the x loads);
-  // tokens >= B keep nothing, the dense product keeps everything
+  // (read out only after every load above has been issued)
+  __builtin_amdgcn_sched_barrier(0);
   uint32_t gk[16];
   int gj[16];
-  // (unconditional loads from a clamped index: all in flight together)
-  const uint64_t* gp = (const uint64_t*)gout;  // GateOut: kthr, jlast first
 #pragma unroll
   for (int b = 0; b < 16; ++b) {
-    const uint64_t g = gp[(size_t)(b < B ? b : 0) * (sizeof(sl::GateOut) / 8)];
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)gpair, b);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(gpair >> 32), b);
     const bool tok = b < B;
-    gk[b] = !tok ? 0xffffffffu : dense ? 0u : (uint32_t)g;
-    gj[b] = !tok ? -1 : dense ? n : (int)(uint32_t)(g >> 32);
+    gk[b] = !tok ? 0xffffffffu : dense ? 0u : lo;
+    gj[b] = !tok ? -1 : dense ? n : (int)hi;
   }
 #pragma unroll
   for (int q = 0; q < ROUNDS; ++q) {
@@ -217,7 +225,7 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
   // are chunk columns 0, 1, ... (the union list is ascending and distinct, so
   // its last entry there decides); steps past cnt are padding (zero inputs)
   const int L = min(cnt, D * UK);
-  const bool held = spec && (L == 0 || ulist[L - 1] == L - 1);
+  const bool held = SPEC && (L == 0 || ulist[L - 1] == L - 1);
 #pragma unroll
   for (int d = 0; d < D; ++d)
     if (d < nsteps && !held) gload(d, d);
@@ -307,9 +315,14 @@ __global__ __launch_bounds__(UT) void union_kernel(const uint16_t* __restrict__ 
 template <typename YT, bool ATOMIC, int NB, int D>
 hipError_t go_nd(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
                  hipStream_t s) {
-  union_kernel<YT, ATOMIC, NB, D><<<p.tiles * p.splits, UT, 0, s>>>(
-      (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
-      p.chunk, dense, p.spec, h->upartials, h->uctr, (YT*)y);
+  if (p.spec)
+    union_kernel<YT, ATOMIC, NB, D, true><<<p.tiles * p.splits, UT, 0, s>>>(
+        (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
+        p.chunk, dense, h->upartials, h->uctr, (YT*)y);
+  else
+    union_kernel<YT, ATOMIC, NB, D, false><<<p.tiles * p.splits, UT, 0, s>>>(
+        (const uint16_t*)h->Wt, (const uint16_t*)x, h->c, h->gout, (int)h->m, (int)h->n, B, p.tiles, p.splits,
+        p.chunk, dense, h->upartials, h->uctr, (YT*)y);
   return hipGetLastError();
 }
 
@@ -317,7 +330,8 @@ template <typename YT, bool ATOMIC, int NB, int D>
 int per_cu_nd() {
   static const int nb = [] {
     int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, union_kernel<YT, ATOMIC, NB, D>, UT, 0) != hipSuccess) v = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, union_kernel<YT, ATOMIC, NB, D, true>, UT, 0) != hipSuccess)
+      v = 1;
     return std::max(1, v);
   }();
   return nb;
@@ -325,13 +339,13 @@ int per_cu_nd() {
 
 template <typename YT, bool ATOMIC>
 int per_cu(int rows) {
-  return rows == 256 ? per_cu_nd<YT, ATOMIC, 4, 3>() : per_cu_nd<YT, ATOMIC, 2, 4>();
+  return rows == 256 ? per_cu_nd<YT, ATOMIC, 4, 2>() : per_cu_nd<YT, ATOMIC, 2, 4>();
 }
 
 template <typename YT, bool ATOMIC>
 hipError_t go(const sl_linear* h, const sl::UnionPlan& p, const void* x, int B, bool dense, void* y,
               hipStream_t s) {
-  if (p.rows == 256) return go_nd<YT, ATOMIC, 4, 3>(h, p, x, B, dense, y, s);
+  if (p.rows == 256) return go_nd<YT, ATOMIC, 4, 2>(h, p, x, B, dense, y, s);
   return go_nd<YT, ATOMIC, 2, 4>(h, p, x, B, dense, y, s);
 }
 
