@@ -861,8 +861,15 @@ def _two_thread_settings(run_one, seconds, max_units, unit, describe):
         single = {"value": round(d1 / e1, 4), "unit": unit, "cores": 1,
                   "sample": f"{d1} {describe}, {e1:.1f} s"}
     dn, en = _timed_oracle(run_one, half, max_units)
-    return {"value": round(dn / en, 4), "unit": unit, "cores": _oracle_threads(), "kind": "oracle",
-            "sample": f"{dn} {describe}, {en:.1f} s", "single_thread": single, "host": host_cpu_model()}
+    out = {"value": round(dn / en, 4), "unit": unit, "cores": _oracle_threads(), "kind": "oracle",
+           "sample": f"{dn} {describe}, {en:.1f} s", "single_thread": single, "host": host_cpu_model()}
+    if single is not None and single["value"] > 0:
+        ratio = out["value"] / single["value"]
+        out["all_threads_over_one"] = round(ratio, 3)
+        if ratio < 1.25:
+            out["note"] = ("cores is the thread count the oracle was allowed; its rate equals the one-thread "
+                           "rate, so the per-unit work runs effectively on one thread")
+    return out
 
 
 def cpu_baseline(wl, Wh, K, seconds):
