@@ -60,6 +60,10 @@ def parse(argv=None):
     ap.add_argument("--counters-run", action="store_true",
                     help="short eager run for memory-counter passes: 12 + 48 headline forwards "
                          "(K=5504), then three plain 256 MiB device copies; prints one line")
+    ap.add_argument("--timeline", action="store_true",
+                    help="per-workgroup timelines of the fused forward from the timeline build of the library "
+                         "(Llama-2-7B down at K=5504 and K=3853, Phi-4 gate and down with the statistical gate); "
+                         "prints one line of phase times")
     ap.add_argument("--workload", default="llama7b_down",
                     choices=["llama7b_down", "llama3_block", "phi4_ffn_stat", "qwen_ffn_b16", "llama2_ffn_chain",
                              "llama2_ds_decode"],
@@ -187,6 +191,8 @@ def main(argv=None):
         return run_workload(args)
     if args.counters_run:
         return counters_run()
+    if args.timeline:
+        return run_timeline()
     return run_headline(args)
 
 
@@ -773,6 +779,116 @@ def run_ds_decode(args):
            "legs": legs, "device": torch.cuda.get_device_name(0)}
     res["cpu_baseline"] = None if args.no_cpu else ds_cpu_baseline(base, min(args.cpu_seconds, 10.0))
     print(json.dumps(res))
+
+
+# Slots of the fused forward's timestamps (sparse_linear_set_timeline).
+TL_GATE = {"keys": 3, "first_barrier": 7, "histogram": 8, "pivot_bin": 9, "candidates": 10, "ranked": 11,
+           "parts_in": 4, "totals_summed": 12, "threshold_computed": 13, "threshold": 5, "selected": 6,
+           "published": 1, "acks_in": 2}
+TL_PROD = {"part_stored": 23, "compacted": 1, "early_poll_back": 2, "pair_polled": 3, "end": 22}
+
+
+def timeline_summary(launches):
+    """Per-phase times (us since the launch's first workgroup started) from
+    [launch][workgroup][32] timestamp arrays (workgroup 0 = the gate): the
+    gate's phases as medians over launches, the product workgroups' as
+    medians over launches of their p10 / median / p90 / max."""
+    import numpy as np
+
+    gate = {k: [] for k in TL_GATE}
+    prod = {k: {"p10": [], "median": [], "p90": [], "max": []} for k in list(TL_PROD) + ["wave_end_max"]}
+    hits, nwg = [], []
+    for a in launches:
+        a = a.astype(np.int64)
+        n = int((a[:, 0] != 0).sum())
+        a = a[:n]
+        base = a[:, 0].min()
+        us = lambda v: (v - base) * 0.01  # s_memrealtime: 100 MHz
+        for k, slot in TL_GATE.items():
+            if a[0, slot] != 0:
+                gate[k].append(us(a[0, slot]))
+        p = a[1:]
+        cols = {k: p[:, slot] for k, slot in TL_PROD.items()}
+        cols["wave_end_max"] = p[:, 4:20].max(axis=1)
+        for k, v in cols.items():
+            v = v[v != 0]
+            if v.size:
+                t = us(v)
+                for q, f in (("p10", 10), ("median", 50), ("p90", 90)):
+                    prod[k][q].append(float(np.percentile(t, f)))
+                prod[k]["max"].append(float(t.max()))
+        seen = p[:, 2] != 0
+        if seen.any():
+            hits.append(float((p[seen, 20] != 0).mean()))
+        nwg.append(n)
+    med = lambda xs: round(float(np.median(xs)), 2) if xs else None
+    return {"workgroups": int(np.median(nwg)),
+            "gate_us": {k: med(v) for k, v in gate.items() if v},
+            "product_us": {k: {q: med(x) for q, x in v.items()} for k, v in prod.items() if v["median"]},
+            "early_poll_saw_pair": med(hits)}
+
+
+def run_timeline():
+    """Timelines of the fused forward (timeline build of the library): 16
+    launches per case after the ring is primed, each with the timestamp
+    buffer installed alone; plus the same build's graph-replay launch time
+    without the buffer (the timestamps' own cost shows against the regular
+    library's time)."""
+    import numpy as np
+    import torch
+
+    import free_activation_sparse_amd as fas
+    from free_activation_sparse_amd import build as fbuild
+    import workloads as wl
+
+    fas.LIB_PATH = fbuild.LIB_TIMELINE
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    buf = torch.zeros(1024 * 32, dtype=torch.int64, device=dev)
+    cases = [("llama7b_down_topk50", 2, 0, dict(gate="topk", K=wl.k_from_sparsity(11008, 0.5))),
+             ("llama7b_down_topk65", 2, 0, dict(gate="topk", K=wl.k_from_sparsity(11008, 0.65))),
+             ("phi4_gate_stat10", 4, 0, dict(gate="stat", s_keep=0.10)),
+             ("phi4_down_stat10", 4, 2, dict(gate="stat", s_keep=0.10))]
+    out = {"timeline": "fused_kernel", "clock": "s_memrealtime (100 MHz)", "cases": {}}
+    weights = {}
+    for name, cfg, li, gk in cases:
+        lin = wl.CONFIGS[cfg].linears[li]
+        m, n = lin.m, lin.n
+        if (cfg, li) not in weights:
+            weights[(cfg, li)] = torch.from_numpy(np.ascontiguousarray(wl.weight(cfg, li)).view(np.int16)).to(dev) \
+                .view(torch.bfloat16)
+        R = max(2, -(-(1 << 30) // (m * n * 2)))
+        ring = [fas.SparseLinear(weights[(cfg, li)], c=None, **gk) for _ in range(R)]
+        X = torch.from_numpy(wl.tokens(cfg, li, 0, 64).view(np.int16)).to(dev).view(torch.bfloat16).contiguous()
+        Y = torch.zeros((R, m), dtype=torch.float32, device=dev)
+
+        def f(i, s):
+            fas.sparse_linear_forward(ring[i % R].handle, X[i % 64].data_ptr(), 1, Y[i % R].data_ptr(), fas.SL_F32,
+                                      0, 0, 0, s)
+        prime(torch, f, 2 * R)
+        launch_us = graph_us(torch, f, count=240)
+        s = torch.cuda.current_stream().cuda_stream
+        launches = []
+        for i in range(2 * R, 2 * R + 16):
+            buf.zero_()
+            torch.cuda.synchronize()
+            fas.sparse_linear_set_timeline(buf.data_ptr())
+            f(i, s)
+            torch.cuda.synchronize()
+            fas.sparse_linear_set_timeline(0)
+            launches.append(buf.view(1024, 32).cpu().numpy().copy())
+        for h in ring:
+            h.sync_status()
+            h.close()
+        res = timeline_summary(launches)
+        res.update({"m": m, "n": n, "gate": gk, "launch_us_graph": round(launch_us, 3)})
+        out["cases"][name] = res
+        print(f"[timeline] {name}: launch {launch_us:.2f} us, published at {res['gate_us'].get('published')} us",
+              file=sys.stderr, flush=True)
+        del ring, X, Y
+        torch.cuda.empty_cache()
+    out["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(out))
 
 
 def counters_run():

@@ -35,7 +35,7 @@ EXPORTED = [
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
     "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
     "sparse_linear_forward_ffn_noalloc",
-    "sparse_linear_gather_ceiling", "ds_label_cache_update", "ds_decode_attention",
+    "sparse_linear_gather_ceiling", "sparse_linear_set_timeline", "ds_label_cache_update", "ds_decode_attention",
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -97,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_sync_status.restype = ctypes.c_int
     L.sparse_linear_gather_ceiling.argtypes = [_vp, _vp, _i32, _vp, _vp]
     L.sparse_linear_gather_ceiling.restype = ctypes.c_int
+    L.sparse_linear_set_timeline.argtypes = [_vp]
+    L.sparse_linear_set_timeline.restype = ctypes.c_int
     L.ds_label_cache_update.argtypes = [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]
     L.ds_label_cache_update.restype = ctypes.c_int
     L.ds_decode_attention.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -203,6 +205,10 @@ def sparse_linear_forward_stages(h: int, x_ptr: int, B: int, y_ptr: int, y_dtype
 def sparse_linear_gather_ceiling(h: int, idx_ptr: int, count: int, sink_ptr: int, stream: int = 0) -> None:
     _check(lib().sparse_linear_gather_ceiling(h, idx_ptr, count, sink_ptr, stream or None),
            "sparse_linear_gather_ceiling")
+
+
+def sparse_linear_set_timeline(buf_ptr: int) -> None:
+    _check(lib().sparse_linear_set_timeline(buf_ptr or None), "sparse_linear_set_timeline")
 
 
 def sparse_linear_set_deterministic(h: int, on: bool) -> None:

@@ -1,4 +1,7 @@
-"""Builds libsparse_linear.so (HIP, gfx950) in-tree with hipcc.
+"""Builds libsparse_linear.so (HIP, gfx950) in-tree with hipcc, and beside
+it libsparse_linear_timeline.so: the same library with fused.hip compiled with
+SL_TIMELINE, whose fused forward records per-workgroup timestamps
+(sparse_linear_set_timeline; measurement only).
 
     python -m free_activation_sparse_amd.build        # always recompiles
 """
@@ -14,6 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_linear.so")
+LIB_TIMELINE = os.path.join(HERE, "libsparse_linear_timeline.so")
 SOURCES = ["api.cpp", "layout.hip", "gate.hip", "product.hip", "fused.hip", "union_product.hip", "ffn.hip", "double_sparse.hip", "ceiling.hip"]
 
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -30,29 +34,38 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(job) -> str:
+    src, defines, suffix = job
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + suffix + ".o")
+    cmd = [HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link both shared libraries; returns the path
+    of the regular one."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    jobs = [(s, [], "") for s in srcs] + [("fused.hip", ["-DSL_TIMELINE"], "_timeline")]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(jobs))) as ex:
+        objs = list(ex.map(_compile, jobs))
+    regular, timeline = objs[:len(srcs)], objs[len(srcs):]
+    _link(regular, LIB)
+    _link([o for o, s in zip(regular, srcs) if s != "fused.hip"] + timeline, LIB_TIMELINE)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {LIB_TIMELINE}")
     return LIB
 
 

@@ -613,6 +613,15 @@ sl_status sparse_linear_gather_ceiling(sl_handle h, const int32_t* idx, int32_t 
   }
 }
 
+sl_status sparse_linear_set_timeline(void* buf) {
+  g_last_error.clear();
+  const hipError_t e = sl::timeline_set(buf);
+  if (e == hipErrorNotSupported)
+    return fail(SL_ERR_UNSUPPORTED, "this library was built without the fused forward's timestamps");
+  SL_HIP(e);
+  return SL_OK;
+}
+
 sl_status sparse_linear_set_deterministic(sl_handle h, int32_t on) {
   if (h == nullptr) return fail(SL_ERR_ARG, "handle is NULL");
   h->deterministic = (on != 0);

@@ -4,6 +4,31 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Per-workgroup timestamps of the fused forward, compiled in only for the
+// timeline build of the library (fused.hip compiled with SL_TIMELINE): word
+// 32 * b + slot of the buffer that sparse_linear_set_timeline installs gets
+// workgroup b's value for that slot. In every other build the macros expand
+// to nothing and their arguments are not evaluated.
+// A function that records declares SL_TL_DECL once at its top: the buffer
+// address is then read once, before the weight stream starts, and kept in a
+// register (read at every point, it was reloaded after each barrier, and each
+// reload waited behind the stream).
+#ifdef SL_TIMELINE
+static __device__ unsigned long long* sl_timeline_buf = nullptr;
+#define SL_TL_DECL unsigned long long* const sl_tl_ = sl_timeline_buf
+#define SL_TL_AT(slot, cond, value)                                                    \
+  do {                                                                                  \
+    if (sl_tl_ != nullptr && (cond)) sl_tl_[(size_t)blockIdx.x * 32 + (slot)] = (value); \
+  } while (0)
+#define SL_TL_WAIT() __builtin_amdgcn_s_waitcnt(0)
+#else
+#define SL_TL_DECL ((void)0)
+#define SL_TL_AT(slot, cond, value) ((void)0)
+#define SL_TL_WAIT() ((void)0)
+#endif
+// thread 0's clock (100 MHz) at this point
+#define SL_TL(slot) SL_TL_AT(slot, threadIdx.x == 0, __builtin_amdgcn_s_memrealtime())
+
 namespace sl {
 namespace dev {
 

@@ -106,6 +106,8 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
   YT* __restrict__ y = a.y;
   const int t = threadIdx.x;
   const int nprod = tiles * splits;
+  SL_TL_DECL;
+  SL_TL(0);
   {
     uint32_t kthr;
     int jlast;
@@ -118,6 +120,7 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
                                               sm.g.dsum, sm.g.kminmax, 0, pin, kthr, jlast);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
     __syncthreads();
+    SL_TL(1);
     if (t == 0) __hip_atomic_store(&sync->flag, pack_gate(kthr, jlast), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (t < 64) {
       // wavefront 0 sums the acknowledgement slots until every product
@@ -132,6 +135,7 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
         if (total >= (uint32_t)nprod || ++it >= kSpinLimit) break;
         __builtin_amdgcn_s_sleep(8);
       }
+      SL_TL(2);
       if (t == 0 && total < (uint32_t)nprod) __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (t < sl::kAckSlots) __hip_atomic_store(&sync->ack[16 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t == 0) __hip_atomic_store(&sync->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -158,6 +162,8 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
   uint32_t* __restrict__ ctr = a.ctr;
   YT* __restrict__ y = a.y;
   const int t = threadIdx.x;
+  SL_TL_DECL;
+  SL_TL(0);
   const int tile = pw % tiles;
   const int split = pw / tiles;
   const int j0 = split * chunk;
@@ -195,6 +201,7 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
         __hip_atomic_store(&sync->parts[(j0 >> 6) + w].w[lane], ((uint64_t)(gen + 1u) << 32) | pl,
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
+      SL_TL_AT(23, lane == 0, __builtin_amdgcn_s_memrealtime());
     }
   }
   sl::proddev::Acc<WT> acc;
@@ -224,6 +231,8 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
   if (g0 != 0xffffffffu) cnt0 = sl::proddev::compact_chunk<FT, false>(ch, j0, j1, g0 - 1u, -1, sm.p.list, sm.p.wcnt);
   constexpr int STEP = sl::proddev::step_columns<LPC, 8, FT>();
   const int nsteps = (cnt0 + STEP - 1) / STEP;  // workgroup-uniform
+  SL_TL(1);
+  SL_TL_AT(21, t == 0, (unsigned long long)cnt0);
 
   // The speculative list, over all wavefronts' column slots. Each wavefront
   // issues its poll of the flag just before its last step's loads: loads
@@ -242,6 +251,8 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
     sl::proddev::step_issue<WT, LPC, 8, FT>(Wt, m, tile, sm.p.list, cnt0, nsteps - 1, last);
     pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pv >> 32), 0) << 32) |
          (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pv, 0);
+    SL_TL(2);
+    SL_TL_AT(20, t == 0, pv);
     uint64_t bal = 0ull;
     bool any = false;
     if (pv != 0ull && g0 > (uint32_t)pv) {  // pair known and the speculation holds
@@ -293,6 +304,7 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
       pv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pv >> 32), 0) << 32) |
            (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pv, 0);
       if (pv == kGateTimeout) pv = 0ull;
+      SL_TL(3);
     }
     if (pv != 0ull) {  // (0: the wait timed out, recorded in the error word)
       const uint32_t kthr = (uint32_t)pv;
@@ -311,12 +323,15 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
       sl::proddev::stream_wave_bits<WT, LPC, 8>(Wt, m, tile, jw, __ballot(rest), ch.xv[0], acc);
     }
   }
+  SL_TL_AT(4 + w, lane == 0, __builtin_amdgcn_s_memrealtime());
   if (t == 0) {
     if (pv == 0ull) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
     __hip_atomic_fetch_add(&sync->ack[16 * (pw % sl::kAckSlots)], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   sl::proddev::reduce_out<WT, YT, LPC, FT, ATOMIC>(acc, m, tile, split, splits, sm.p.red, partials, ctr,
                                                    &sm.p.s_last, y);
+  SL_TL_WAIT();
+  SL_TL(22);
 }
 
 // One linear: workgroup 0 is the gate, 1.. the product.
@@ -526,6 +541,15 @@ hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void*
   if (groups <= 5) return go_group_mode<5>(hs, count, x, ys, s);
   if (groups <= 6) return go_group_mode<6>(hs, count, x, ys, s);
   return go_group_mode<8>(hs, count, x, ys, s);
+}
+
+hipError_t timeline_set(void* buf) {
+#ifdef SL_TIMELINE
+  return hipMemcpyToSymbol(HIP_SYMBOL(sl_timeline_buf), &buf, sizeof(buf));
+#else
+  (void)buf;
+  return hipErrorNotSupported;
+#endif
 }
 
 bool fused_supported(const sl_linear* h, const void* x) {

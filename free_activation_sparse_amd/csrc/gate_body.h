@@ -335,6 +335,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
                                           uint32_t* res, uint64_t* cand, sd (*dsum)[2],
                                           uint32_t (*kminmax)[2], int b, PartsIn pin, uint32_t& kthr_out,
                                           int& jlast_out) {
+  SL_TL_DECL;
   constexpr int E = 4 * G;
   const int t = threadIdx.x, lane = t & 63, w = wave_id();
   const XT* xb = x + (size_t)b * n;
@@ -378,12 +379,14 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
 #pragma unroll
       for (int e = 0; e < E; ++e) lmax = max(lmax, key[e]);  // padding keys are 0
       lmax = wave_max(lmax);
+      SL_TL(3);  // wavefront 0's keys are in
       if (lane == 0) wsum[w] = lmax;
       if (t == 0) {
         res[0] = 0xffffffffu;  // "not found" unless find_bin writes it
         res[3] = 0u;           // candidate counter
       }
       __syncthreads();  // h1 cleared, maxima and res published
+      SL_TL(7);
       uint32_t kmax = wsum[0];
 #pragma unroll
       for (int k = 1; k < GW; ++k) kmax = max(kmax, wsum[k]);
@@ -398,12 +401,14 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
         if (d < 4096u) atomicAdd(&h1[d], 1u);
       }
       __syncthreads();
+      SL_TL(8);
       // fewer reads in flight when the keys take many registers
       if (w == 0)
         find_bin_wave<4096, (E <= 16 ? 8 : 2)>(h1, (uint32_t)K, res);
       else
         clear_y(1);
       __syncthreads();
+      SL_TL(9);
       const bool in_window = res[0] != 0xffffffffu;
       const uint32_t c1 = in_window ? res[2] : 0u;
       if (in_window && c1 <= 64u) {
@@ -431,6 +436,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           }
         }
         __syncthreads();
+        SL_TL(10);
         // rank of each candidate among the c1, by wavefront 0 (lane a holds
         // candidate a and compares it with every other through readlane)
         if (w == 0) {
@@ -448,6 +454,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           }
         }
         __syncthreads();
+        SL_TL(11);
         kthr = res[1];
         jlast = (int)res[2];
       } else {
@@ -511,6 +518,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       uint32_t kmin = 0xffffffffu, kmax = 0u;
       const dd inv_n = dd_recip((double)n);  // early: its divisions stay off the final chain
       bool local = pin.parts == nullptr;
+      bool summed = false;  // the parts' totals are already complete in every lane of wavefront 0
       if (!local) {
         // parts of every 64-input slice, part q in lane q mod 64 of
         // wavefront q / 64: each such wavefront polls until all of its parts
@@ -556,15 +564,26 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           }
         }
         __syncthreads();
+        SL_TL(4);  // every moment part is in (or the wait gave up)
         all = true;
         for (int k = 0; k < nw; ++k) all &= wsum[k] != 0u;
         if (all && w == 0) {
-          S1 = lane < nw ? dsum[lane][0] : sd{0.0, 0.0};
-          S2 = lane < nw ? dsum[lane][1] : sd{0.0, 0.0};
-          kmin = lane < nw ? kminmax[lane][0] : 0xffffffffu;
-          kmax = lane < nw ? kminmax[lane][1] : 0u;
+          // the nw (<= 8) polling wavefronts' totals, added in order by
+          // every lane: nw - 1 dependent additions instead of the four
+          // levels of a 16-lane scan
+          S1 = dsum[0][0];
+          S2 = dsum[0][1];
+          kmin = kminmax[0][0];
+          kmax = kminmax[0][1];
+          for (int k = 1; k < nw; ++k) {
+            S1 = sd_add(S1, dsum[k][0]);
+            S2 = sd_add(S2, dsum[k][1]);
+            kmin = min(kmin, kminmax[k][0]);
+            kmax = max(kmax, kminmax[k][1]);
+          }
         }
         local = !all;
+        summed = all;
       }
       if (local) {
         // this workgroup's scores: per-thread sums, per-wavefront totals,
@@ -597,10 +616,13 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       }
       clear_y(1);
       if (w == 0) {
-        // the wavefront totals sit in lanes 0..15 (nothing above)
-        row0_sum_sd(S1, S2);
-        kmax = wave_max(kmax);
-        kmin = ~wave_max(~kmin);
+        if (!summed) {
+          // the wavefront totals sit in lanes 0..15 (nothing above)
+          row0_sum_sd(S1, S2);
+          kmax = wave_max(kmax);
+          kmin = ~wave_max(~kmin);
+        }
+        SL_TL(12);  // wavefront totals summed
         if (lane == 0) {
           const dd T1 = fast_two_sum(S1.hi, S1.lo), T2 = fast_two_sum(S2.hi, S2.lo);
           const dd mu = dd_mul(T1, inv_n);
@@ -624,8 +646,10 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           res[1] = (uint32_t)jl;
           dsum[0][0].hi = tt;
         }
+        SL_TL(13);  // mu, sigma, t and the key pair computed
       }
       __syncthreads();
+      SL_TL(5);  // threshold known
       kthr = res[0];
       jlast = (int)res[1];
       thresh = dsum[0][0].hi;
@@ -664,6 +688,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
     if (count_out != nullptr) count_out[b] = count;
     if (thresh_out != nullptr) thresh_out[b] = thresh;
   }
+  SL_TL(6);
   kthr_out = kthr;
   jlast_out = jlast;
 }

@@ -150,6 +150,10 @@ hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void*
 // Fused gate + product for one token (bf16 weights, any gate, n % 4 == 0 and
 // x 8-byte aligned: fused_supported).
 bool fused_supported(const sl_linear* h, const void* x);
+// Installs (or, with nullptr, removes) the per-workgroup timestamp buffer of
+// the fused forward; hipErrorNotSupported unless fused.hip was compiled with
+// SL_TIMELINE (the timeline build of the library).
+hipError_t timeline_set(void* buf);
 hipError_t launch_fused(const sl_linear* h, const void* x, GateOut* g, uint8_t* mask_out, int32_t* count_out,
                         double* thresh_out, void* y, sl_dtype ydt, bool atomic, hipStream_t s);
 // Double Sparsity decode attention (layouts and semantics in double_sparse.h).

@@ -265,6 +265,26 @@ sl_status sparse_linear_forward_stages(sl_handle h, const void* x, int32_t B, vo
 sl_status sparse_linear_gather_ceiling(sl_handle h, const int32_t* idx, int32_t count, float* sink, void* stream);
 
 /*
+ * sparse_linear_set_timeline -- measurement only: installs buf (device
+ * uint64[32 * workgroups], caller-owned, zeroed by the caller) as the
+ * per-workgroup timestamp buffer of the fused single-token forward, or
+ * removes it (buf == NULL). While installed, every fused launch writes, for
+ * workgroup b, the 100 MHz clock (s_memrealtime) at named points into word
+ * 32 * b + slot: gate workgroup (b = 0): 0 start, 3 keys in, 7/8/9/10/11 the
+ * top-K phases (first barrier, histogram, pivot bin, candidates, ranked),
+ * 4 moment parts in, 12 their totals summed, 13 mu, sigma and t computed
+ * (one lane) and 5 threshold known (statistical gate), 6 selection
+ * done, 1 pair published, 2 acknowledgements in; product workgroups: 0 start,
+ * 23 moment part stored, 1 speculative list compacted (21: its length),
+ * 2 early poll back (20: the value it read), 3 pair seen by the second poll,
+ * 4 + w end of wavefront w's stream, 22 end. Only the timeline build of the
+ * library (libsparse_linear_timeline.so) records anything; the regular
+ * library returns SL_ERR_UNSUPPORTED. Timestamps add a few stores per
+ * workgroup, so absolute times run ~10 % above an uninstrumented launch.
+ */
+sl_status sparse_linear_set_timeline(void* buf);
+
+/*
  * Split reduction mode. The product kernel splits the kept inputs into chunks
  * whose partial sums are added per output row. By default (on == 0) fp32
  * outputs take fp32 atomic adds, which is fastest but lets the summation order

@@ -173,3 +173,22 @@ def test_ds_label_update_rejects(slib):
     assert f(d=32) == 2 and f(r=4) == 2 and f(S=0) == 1 and f(span=-1) == 1
     assert f(label=_P + 4) == 2 and f(start=_P + 2) == 1
     assert f(span=0) == 0          # nothing to do: no device access
+
+
+def test_timeline_setter_unsupported_in_regular_build(slib):
+    """The regular library has no timestamp points: installing a buffer is
+    refused without touching a device."""
+    st = slib.lib().sparse_linear_set_timeline(None)
+    assert st == slib.SL_ERR_UNSUPPORTED
+    assert "timestamps" in slib.sparse_linear_last_error()
+
+
+def test_timeline_library_exports_every_declared_symbol(slib):
+    """The timeline build (fused.hip with its timestamp points) is the same
+    ABI; it loads without a device."""
+    from free_activation_sparse_amd import build as _build
+    if not os.path.exists(_build.LIB_TIMELINE):
+        _build.build()
+    L = ctypes.CDLL(_build.LIB_TIMELINE)
+    for name in _declared():
+        assert hasattr(L, name), name

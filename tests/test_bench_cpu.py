@@ -57,3 +57,36 @@ def test_parse_defaults_and_legs():
     assert a.gpus == 1 and a.workload == "llama7b_down" and a.only == "all"
     for leg in ("sparse50", "sparse65", "fixed50", "dense", "ceiling"):
         assert bench.parse(["--only", leg]).only == leg
+
+
+def test_timeline_summary_phases():
+    """Phase times from synthetic timestamp arrays: microseconds since the
+    launch's first workgroup started (100 MHz clock), the gate's slots as
+    medians over launches, the product workgroups' percentiles, and the
+    fraction of early polls that returned the pair."""
+    import numpy as np
+    import bench
+    launches = []
+    for L in range(3):
+        a = np.zeros((8, 32), dtype=np.int64)
+        base = 1000 + 50 * L
+        a[0, 0] = base + 10             # gate starts 0.1 us after the first product workgroup
+        a[0, 3] = base + 100
+        a[0, 1] = base + 500            # published at 5 us
+        a[0, 2] = base + 900
+        for w in range(1, 6):
+            a[w, 0] = base + (0 if w == 1 else 20)
+            a[w, 1] = base + 120
+            a[w, 2] = base + 700
+            a[w, 20] = 1 if w <= 2 else 0   # 2 of 5 early polls saw the pair
+            a[w, 4:20] = base + 800 + 10 * w
+            a[w, 22] = base + 900 + 10 * w
+        launches.append(a)
+    res = bench.timeline_summary(launches)
+    assert res["workgroups"] == 6
+    assert res["gate_us"]["published"] == 5.0 and res["gate_us"]["keys"] == 1.0
+    assert "parts_in" not in res["gate_us"]
+    assert res["product_us"]["compacted"]["median"] == 1.2
+    assert res["product_us"]["end"]["max"] == 9.5
+    assert res["product_us"]["wave_end_max"]["max"] == 8.5
+    assert res["early_poll_saw_pair"] == 0.4
