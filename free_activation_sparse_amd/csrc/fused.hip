@@ -33,7 +33,6 @@ using namespace sl::dev;
 constexpr int FT = sl::gatedev::GT;  // threads per workgroup (16 wavefronts)
 constexpr uint32_t kSpinLimit = 1u << 20;  // polls (>= 50 ns each) before giving up
 constexpr float kSpecMargin = 1.15f;       // speculation bound over the previous threshold score
-constexpr uint32_t kPartsWait = 2000;      // s_memrealtime ticks (20 us) the gate waits for moment parts
 
 struct GateSmem {
   alignas(16) uint32_t h1[4096];
@@ -82,7 +81,6 @@ struct FusedArgs {
   uint32_t* ctr;
   sl::FusedSync* sync;
   uint32_t* err;  // host-visible record of a timed-out wait (system scope)
-  int use_parts;
   YT* y;
 };
 
@@ -98,7 +96,7 @@ template <typename WT, typename YT, int G, int MODE, int LPC, bool ATOMIC>
 __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT* __restrict__ x, int n,
                                            FusedSmem<WT>& sm) {
   const float* __restrict__ c = a.c;
-  const int m = a.m, K = a.K, tiles = a.tiles, splits = a.splits, use_parts = a.use_parts;
+  const int m = a.m, K = a.K, tiles = a.tiles, splits = a.splits;
   const double z = a.z;
   const float tau = a.tau;
   sl::GateOut* __restrict__ gout = a.gout;
@@ -112,12 +110,9 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
     uint32_t kthr;
     int jlast;
     float* zy = (ATOMIC && splits > 1) ? (float*)y : nullptr;
-    const uint32_t gen = __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sl::gatedev::PartsIn pin{};
-    if (MODE == sl::gatedev::MODE_STAT && use_parts) pin = {sync->parts, (n + 63) / 64, gen + 1u, kPartsWait};
     sl::gatedev::gate_body<WT, G, MODE, true>(x, c, n, K, z, tau, gout, a.mask_out, a.count_out, a.thresh_out, zy, m,
                                               sm.g.h1, sm.g.h2, sm.g.h3, sm.g.wsum, sm.g.res, sm.g.cand,
-                                              sm.g.dsum, sm.g.kminmax, 0, pin, kthr, jlast);
+                                              sm.g.dsum, sm.g.kminmax, 0, kthr, jlast);
     __builtin_amdgcn_s_waitcnt(0);  // this thread's clearing stores are complete
     __syncthreads();
     SL_TL(1);
@@ -139,9 +134,6 @@ __device__ __forceinline__ void fused_gate(const FusedArgs<WT, YT>& a, const WT*
       if (t == 0 && total < (uint32_t)nprod) __hip_atomic_store(a.err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (t < sl::kAckSlots) __hip_atomic_store(&sync->ack[16 * slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (t == 0) __hip_atomic_store(&sync->flag, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      // a new tag for the next launch's moment parts: anything written
-      // under this one (late or not) no longer counts
-      if (t == 0) __hip_atomic_store(&sync->gen, gen + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -154,7 +146,7 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
                                               FusedSmem<WT>& sm) {
   const WT* __restrict__ Wt = a.Wt;
   const float* __restrict__ c = a.c;
-  const int m = a.m, tiles = a.tiles, splits = a.splits, chunk = a.chunk, use_parts = a.use_parts;
+  const int m = a.m, tiles = a.tiles, splits = a.splits, chunk = a.chunk;
   const float tau = a.tau;
   sl::GateOut* __restrict__ gout = a.gout;
   sl::FusedSync* __restrict__ sync = a.sync;
@@ -171,39 +163,11 @@ __device__ __forceinline__ void fused_product(const FusedArgs<WT, YT>& a, const 
   // the handle's previous threshold key (any value read here is safe: it only
   // steers the speculation below, which is checked against the exact pair)
   const uint32_t prevk = SPEC ? __hip_atomic_load(&gout->kthr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-  // the tag for this launch's moment parts (statistical gate)
-  const uint32_t gen = MODE == sl::gatedev::MODE_STAT && use_parts
-                           ? __hip_atomic_load(&sync->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : 0u;
   static_assert(sl::proddev::Chunk<FT>::ROUNDS == 1, "one input per thread");
   sl::proddev::Chunk<FT> ch;
   sl::proddev::load_chunk<WT, FT, false>(x, c, j0, j1, ch);
   const int lane = t & 63, w = wave_id();
   const int jt = j0 + t;
-  if (MODE == sl::gatedev::MODE_STAT && use_parts) {
-    // Statistical gate: the moment sums of the token's scores come from
-    // here, one part per 64-input slice of the chunk (chunks start at
-    // multiples of 64), each summed by one wavefront of one row tile's
-    // workgroup and stored before the weight stream loads the memory
-    // system; the gate workgroup adds the parts in index order.
-    const int nsl = (j1 - j0 + 63) >> 6;
-    if (w < nsl && w % tiles == tile) {
-      const bool valid = jt < j1;
-      const double s = valid ? (double)__uint_as_float(ch.kv[0]) : 0.0;
-      sl::gatedev::sd S1{s, 0.0}, S2{s * s, 0.0};  // squares of fp32 values are exact in fp64
-      sl::gatedev::wave_sum_sd(S1, S2);
-      const uint32_t kmax = wave_max(valid ? ch.kv[0] : 0u);
-      const uint32_t kmin = ~wave_max(valid ? ~ch.kv[0] : 0u);
-      if (lane < sl::kMomentWords) {
-        // lane k stores word k: payload in the low half, the tag above it
-        const uint64_t d = (uint64_t)__double_as_longlong(lane < 2 ? S1.hi : lane < 4 ? S1.lo : lane < 6 ? S2.hi : S2.lo);
-        const uint32_t pl = lane == 8 ? kmin : lane == 9 ? kmax : (uint32_t)(d >> (32 * (lane & 1)));
-        __hip_atomic_store(&sync->parts[(j0 >> 6) + w].w[lane], ((uint64_t)(gen + 1u) << 32) | pl,
-                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      SL_TL_AT(23, lane == 0, __builtin_amdgcn_s_memrealtime());
-    }
-  }
   sl::proddev::Acc<WT> acc;
 #pragma unroll
   for (int v = 0; v < sl::proddev::Acc<WT>::VEC; ++v) acc.v[v] = 0.f;
@@ -379,7 +343,7 @@ struct FusedPlan {
 // Row tiles of LPC * 8 rows; the input chunks are sized so that the product
 // workgroups fill the device's remaining workgroup slots once (chunks of
 // 32..kMaxChunk inputs), unless a split count is forced on the handle.
-FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu, int align) {
+FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu) {
   FusedPlan p;
   const int64_t n = h->n;
   const int rows = lpc * 8;
@@ -389,7 +353,6 @@ FusedPlan plan_fused(const sl_linear* h, int lpc, int per_cu, int align) {
   splits = std::min<int64_t>(splits, std::min<int64_t>(sl::kMaxSplits, (n + 31) / 32));
   splits = std::max<int64_t>(splits, (n + sl::kMaxChunk - 1) / sl::kMaxChunk);
   p.chunk = (int)((n + splits - 1) / splits);
-  p.chunk = (p.chunk + align - 1) / align * align;  // kMaxChunk is a multiple of align
   p.splits = (int)((n + p.chunk - 1) / p.chunk);
   return p;
 }
@@ -404,14 +367,9 @@ hipError_t go(const sl_linear* h, const void* x, sl::GateOut* g, uint8_t* mask, 
       nb = 1;
     return std::max(1, nb);
   }();
-  // the statistical gate's moment parts cover 64-input slices that must not straddle chunks
-  const FusedPlan p = plan_fused(h, LPC, per_cu, MODE == sl::gatedev::MODE_STAT ? 64 : 1);
-  // moment parts only when every workgroup of the launch can be resident at
-  // once (the gate would otherwise wait for workgroups not yet dispatched)
-  const int use_parts = 1 + (int64_t)p.tiles * p.splits <= (int64_t)std::max(1, h->cus) * per_cu ? 1 : 0;
+  const FusedPlan p = plan_fused(h, LPC, per_cu);
   const FusedArgs<uint16_t, YT> a{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau, g, mask, cnt,
-                                 th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, h->herr_dev, use_parts,
-                                 (YT*)y};
+                                 th, p.tiles, p.splits, p.chunk, h->partials, h->ctr, h->fsync, h->herr_dev, (YT*)y};
   fused_kernel<uint16_t, YT, G, MODE, LPC, ATOMIC><<<1 + p.tiles * p.splits, FT, 0, s>>>(a, (const uint16_t*)x,
                                                                                           (int)h->n);
   return hipGetLastError();
@@ -489,25 +447,20 @@ hipError_t go_group(const sl_linear* const* hs, int count, const void* x, float*
   FusedGroup<uint16_t> gr{};
   gr.count = count;
   int64_t total = 0;
-  const int align = MODE == sl::gatedev::MODE_STAT ? 64 : 1;
   for (int l = 0; l < count; ++l) {
     const sl_linear* h = hs[l];
     int64_t splits = (int64_t)((double)slots * wl[l] / wsum) / tiles[l];
     splits = std::min(std::max(splits, (int64_t)1), max_splits);
     splits = std::max(splits, min_splits);
-    int chunk = (int)((n + splits - 1) / splits);
-    chunk = (chunk + align - 1) / align * align;
+    const int chunk = (int)((n + splits - 1) / splits);
     splits = (n + chunk - 1) / chunk;
     gr.begin[l] = (int)total;
     gr.lin[l] = FusedArgs<uint16_t, float>{(const uint16_t*)h->Wt, h->c, (int)h->m, (int)h->K, h->z, h->tau,
                                            h->gout, nullptr, nullptr, nullptr, (int)tiles[l], (int)splits, chunk,
-                                           h->partials, h->ctr, h->fsync, h->herr_dev, 0, ys[l]};
+                                           h->partials, h->ctr, h->fsync, h->herr_dev, ys[l]};
     total += tiles[l] * splits;
   }
   gr.begin[count] = (int)total;
-  // moment parts only when the whole grid is resident at once
-  const int use_parts = count + total <= (int64_t)std::max(1, hs[0]->cus) * per_cu ? 1 : 0;
-  for (int l = 0; l < count; ++l) gr.lin[l].use_parts = use_parts;
   fused_group_kernel<uint16_t, G, MODE, LPC><<<(unsigned)(count + total), FT, 0, s>>>(gr, (const uint16_t*)x, (int)n);
   return hipGetLastError();
 }

@@ -27,10 +27,10 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
   int jlast;
   if (vec)
     gate_body<XT, G, MODE, true>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2, h3,
-                                 wsum, res, cand, dsum, kminmax, blockIdx.x, PartsIn{}, kthr, jlast);
+                                 wsum, res, cand, dsum, kminmax, blockIdx.x, kthr, jlast);
   else
     gate_body<XT, G, MODE, false>(x, c, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2,
-                                  h3, wsum, res, cand, dsum, kminmax, blockIdx.x, PartsIn{}, kthr, jlast);
+                                  h3, wsum, res, cand, dsum, kminmax, blockIdx.x, kthr, jlast);
 }
 
 template <typename XT, int G>

@@ -269,16 +269,6 @@ __device__ __forceinline__ void thread_moments(const uint32_t (&key)[E], uint32_
   S2 = {a2 - sig2, e2};
 }
 
-// Moment parts published by other workgroups of the same launch (fused
-// forward). parts == nullptr: the gate workgroup sums its own scores, as it
-// also does when the parts are not all in after wait_ticks.
-struct PartsIn {
-  const sl::MomentPart* parts = nullptr;
-  int count = 0;            // parts expected (slices of 64 inputs)
-  uint32_t tag = 0;         // tag of this launch's parts
-  uint32_t wait_ticks = 0;  // s_memrealtime ticks (100 MHz) before the gate sums its own scores
-};
-
 // Threshold t (>= 0 keeps score > t; < 0 keeps everything) as a key pair.
 __device__ __forceinline__ void thresh_to_key(double t, int n, uint32_t& kthr, int& jlast) {
   if (t < 0.0) {
@@ -333,7 +323,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
                                           double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
                                           uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
                                           uint32_t* res, uint64_t* cand, sd (*dsum)[2],
-                                          uint32_t (*kminmax)[2], int b, PartsIn pin, uint32_t& kthr_out,
+                                          uint32_t (*kminmax)[2], int b, uint32_t& kthr_out,
                                           int& jlast_out) {
   SL_TL_DECL;
   constexpr int E = 4 * G;
@@ -517,77 +507,9 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       sd S1{0.0, 0.0}, S2{0.0, 0.0};
       uint32_t kmin = 0xffffffffu, kmax = 0u;
       const dd inv_n = dd_recip((double)n);  // early: its divisions stay off the final chain
-      bool local = pin.parts == nullptr;
-      bool summed = false;  // the parts' totals are already complete in every lane of wavefront 0
-      if (!local) {
-        // parts of every 64-input slice, part q in lane q mod 64 of
-        // wavefront q / 64: each such wavefront polls until all of its parts
-        // carry this launch's tag, sums them over its lanes, and the
-        // wavefront totals meet in LDS
-        const int nw = (pin.count + 63) >> 6;  // <= GW: n <= 32768
-        const int q = 64 * w + lane;
-        const bool have = q < pin.count;
-        bool all = false;
-        if (w < nw) {
-          // one round trip per poll: every word of the lane's part, each
-          // carrying the writer's tag
-          const uint64_t* pq = pin.parts[have ? q : 0].w;
-          const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + pin.wait_ticks;
-          uint32_t v[sl::kMomentWords];
-          for (;;) {
-            bool in = true;
-#pragma unroll
-            for (int k = 0; k < sl::kMomentWords; ++k) {
-              const uint64_t u = have ? __hip_atomic_load(pq + k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                                      : ((uint64_t)pin.tag << 32) | (k == 8 ? 0xffffffffull : 0ull);
-              v[k] = (uint32_t)u;
-              in &= (uint32_t)(u >> 32) == pin.tag;
-            }
-            all = __ballot(!in) == 0ull;
-            if (all || __builtin_amdgcn_s_memrealtime() > t_end) break;
-            __builtin_amdgcn_s_sleep(1);
-          }
-          auto dbl = [&](int k) {
-            return __longlong_as_double((long long)(((uint64_t)v[k + 1] << 32) | v[k]));
-          };
-          S1 = sd{dbl(0), dbl(2)};
-          S2 = sd{dbl(4), dbl(6)};
-          wave_sum_sd(S1, S2);
-          kmin = ~wave_max(~v[8]);
-          kmax = wave_max(v[9]);
-          if (lane == 0) {
-            wsum[w] = all ? 1u : 0u;
-            dsum[w][0] = S1;
-            dsum[w][1] = S2;
-            kminmax[w][0] = kmin;
-            kminmax[w][1] = kmax;
-          }
-        }
-        __syncthreads();
-        SL_TL(4);  // every moment part is in (or the wait gave up)
-        all = true;
-        for (int k = 0; k < nw; ++k) all &= wsum[k] != 0u;
-        if (all && w == 0) {
-          // the nw (<= 8) polling wavefronts' totals, added in order by
-          // every lane: nw - 1 dependent additions instead of the four
-          // levels of a 16-lane scan
-          S1 = dsum[0][0];
-          S2 = dsum[0][1];
-          kmin = kminmax[0][0];
-          kmax = kminmax[0][1];
-          for (int k = 1; k < nw; ++k) {
-            S1 = sd_add(S1, dsum[k][0]);
-            S2 = sd_add(S2, dsum[k][1]);
-            kmin = min(kmin, kminmax[k][0]);
-            kmax = max(kmax, kminmax[k][1]);
-          }
-        }
-        local = !all;
-        summed = all;
-      }
-      if (local) {
-        // this workgroup's scores: per-thread sums, per-wavefront totals,
-        // then the 16 wavefront totals in wavefront 0
+      {
+        // the token's scores: per-thread sums, per-wavefront totals, then
+        // the 16 wavefront totals in wavefront 0
         uint32_t kall = 0u;
         kmin = 0xffffffffu;
 #pragma unroll
@@ -616,12 +538,10 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       }
       clear_y(1);
       if (w == 0) {
-        if (!summed) {
-          // the wavefront totals sit in lanes 0..15 (nothing above)
-          row0_sum_sd(S1, S2);
-          kmax = wave_max(kmax);
-          kmin = ~wave_max(~kmin);
-        }
+        // the wavefront totals sit in lanes 0..15 (nothing above)
+        row0_sum_sd(S1, S2);
+        kmax = wave_max(kmax);
+        kmin = ~wave_max(~kmin);
         SL_TL(12);  // wavefront totals summed
         if (lane == 0) {
           const dd T1 = fast_two_sum(S1.hi, S1.lo), T2 = fast_two_sum(S2.hi, S2.lo);

@@ -59,29 +59,12 @@ struct UnionPlan {
 // over kAckSlots counters on separate 64-byte lines, so that the product
 // workgroups' atomic increments do not queue on one address.
 constexpr int kAckSlots = 64;
-// Partial moments of one 64-input slice of a token's scores (statistical
-// gate of the fused forward): ten 32-bit payload words (the unnormalised
-// double-double sums of the scores and of their squares as s1_hi, s1_lo,
-// s2_hi, s2_lo, low word first, then the slice's smallest and largest score
-// keys), each stored in the low half of a 64-bit word whose high half is the
-// writing launch's tag. 64-bit stores and loads are single-copy atomic, so a
-// reader that sees its launch's tag in all ten words has the whole part, with
-// no fence or completion wait on either side.
-constexpr int kMomentWords = 10;
-struct MomentPart {
-  uint64_t w[kMomentWords];
-};
-constexpr int kMaxMomentParts = 32768 / 64;  // the fused forward takes n <= 32768
 struct FusedSync {
   uint64_t flag;  // 0, or the kept-set pair: kthr | (jlast + 2) << 32
   uint32_t pad[14];
   uint32_t ack[kAckSlots * 16];  // slot i at ack[16 * i]: product workgroups pw = i mod kAckSlots
-  uint32_t gen;                  // launches completed (mod 2^32), advanced by the gate workgroup at its end
-  uint32_t pad2[15];
-  MomentPart parts[kMaxMomentParts];
 };
-static_assert(sizeof(MomentPart) == 8 * kMomentWords, "MomentPart layout");
-static_assert(sizeof(FusedSync) == 64 + 64 * kAckSlots + 64 + 8 * kMomentWords * kMaxMomentParts, "FusedSync layout");
+static_assert(sizeof(FusedSync) == 64 + 64 * kAckSlots, "FusedSync layout");
 
 }  // namespace sl
 

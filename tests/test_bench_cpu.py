@@ -85,7 +85,7 @@ def test_timeline_summary_phases():
     res = bench.timeline_summary(launches)
     assert res["workgroups"] == 6
     assert res["gate_us"]["published"] == 5.0 and res["gate_us"]["keys"] == 1.0
-    assert "parts_in" not in res["gate_us"]
+    assert "threshold" not in res["gate_us"]
     assert res["product_us"]["compacted"]["median"] == 1.2
     assert res["product_us"]["end"]["max"] == 9.5
     assert res["product_us"]["wave_end_max"]["max"] == 8.5
