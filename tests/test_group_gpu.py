@@ -67,8 +67,9 @@ def test_group_llama3_block_inputs(fas):
 
 
 def test_group_stat_and_fixed(fas):
-    """Statistical gate (moment parts per linear inside one launch) and fixed
-    thresholds, on ragged row counts sharing n."""
+    """Statistical gates (one gate workgroup per linear, each summing its own
+    token's scores, inside one launch) and fixed thresholds, on ragged row
+    counts sharing n."""
     n = 5120
     ms = [1024, 2056, 520]
     Ws = [wl.random_matrix(150 + i, m, n, "bf16") for i, m in enumerate(ms)]

@@ -184,12 +184,11 @@ def test_stat_gate_constant_scores(fas, dtype, fused):
 
 
 def test_stat_fused_plans(fas):
-    """Fused statistical gate under every launch shape: the moment sums come
-    from parts that one wavefront per 64-input slice publishes (row tiles
-    fewer or more than the slices of a chunk), or, when the launch has more
-    workgroups than the device holds at once, from the gate workgroup's own
-    scores. Masks, counts and thresholds equal the oracle's and the two-launch
-    path's."""
+    """Fused statistical gate under every launch shape (row tiles of 128, 256
+    and 512 rows; 1 to 150 input chunks, including more workgroups than the
+    device holds at once and chunks of 34 inputs): the gate workgroup sums the
+    token's scores itself, so masks, counts and thresholds must equal the
+    oracle's and the two-launch path's whatever the product's layout."""
     m, n = 2048, 5000
     W = wl.random_matrix(130, m, n, "bf16")
     c = oracle.column_norms(W)
