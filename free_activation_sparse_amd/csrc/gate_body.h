@@ -141,6 +141,11 @@ __device__ __forceinline__ void find_bin_wave(const uint32_t* hist, uint32_t r, 
   }
 }
 
+// Raw (untyped) buffer resources: word 3 of the descriptor on gfx9 parts, and
+// the cache-policy operand of a buffer access that sets sc1 alone.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kPolicySc1 = 16;
+
 // ---------------------------------------------------------------- double-double
 struct dd {
   double hi, lo;
@@ -182,80 +187,79 @@ __device__ __forceinline__ dd dd_sqr(dd a) {
 }
 
 // ---------------------------------------------------------------- moments
-// Sums of non-negative terms as unnormalised double-double pairs: the high
-// parts add error-free (two_sum), the low parts collect the rounding errors
-// in plain fp64. With no cancellation the relative error stays near 2^-100,
-// far below the single rounding to fp64 that the mean and the variance take.
-struct sd {
-  double hi, lo;
+// Sums of the scores and of their squares, to ~2^-100 relative, far below
+// the single rounding to fp64 that the mean and the variance take. Every
+// thread adds its E scores onto a power-of-two offset sigma >= E * (the
+// workgroup's largest score), the same for all threads: each running sum
+// stays in [sigma, 2 sigma), at or above each addend, so Fast2Sum yields
+// each rounding error exactly (kept in a plain fp64 error sum), and the
+// running sum itself is sigma plus an integer multiple of ulp(sigma), that
+// integer being the mantissa field of its bit pattern. Those integers
+// (< 2^52 per thread, < 2^62 over a workgroup) then add exactly in uint64,
+// and only the tiny error sums round. Squares of fp32 values are exact in
+// fp64; keys of 0 add nothing.
+struct Moments {
+  uint64_t i1, i2;  // sums of the running-sum mantissas (units of ulp(sigma))
+  double e1, e2;    // sums of the rounding errors
 };
-__device__ __forceinline__ sd sd_add(sd a, sd b) {
-  const dd s = two_sum(a.hi, b.hi);
-  return {s.hi, (a.lo + b.lo) + s.lo};
-}
 
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint64_t lo = dpp_move<CTRL>((uint32_t)v), hi = dpp_move<CTRL>((uint32_t)(v >> 32));
+  return (hi << 32) | lo;
+}
 template <int CTRL>
 __device__ __forceinline__ double dpp_f64(double v) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = dpp_move<CTRL>((uint32_t)u), hi = dpp_move<CTRL>((uint32_t)(u >> 32));
-  return __longlong_as_double((long long)((hi << 32) | lo));
+  return __longlong_as_double((long long)dpp_u64<CTRL>((uint64_t)__double_as_longlong(v)));
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l) {
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+  return (hi << 32) | lo;
 }
 __device__ __forceinline__ double readlane_f64(double v, int l) {
-  const uint64_t u = (uint64_t)__double_as_longlong(v);
-  const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
-  const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
-  return __longlong_as_double((long long)((hi << 32) | lo));
+  return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), l));
 }
 template <int CTRL>
-__device__ __forceinline__ void sd_scan_step(sd& a, sd& b, bool take) {
-  const sd ta{dpp_f64<CTRL>(a.hi), dpp_f64<CTRL>(a.lo)};
-  const sd tb{dpp_f64<CTRL>(b.hi), dpp_f64<CTRL>(b.lo)};
-  if (take) {
-    a = sd_add(a, ta);
-    b = sd_add(b, tb);
-  }
+__device__ __forceinline__ void moments_step(Moments& a) {
+  a.i1 += dpp_u64<CTRL>(a.i1);
+  a.i2 += dpp_u64<CTRL>(a.i2);
+  a.e1 += dpp_f64<CTRL>(a.e1);
+  a.e2 += dpp_f64<CTRL>(a.e2);
 }
-// Wavefront totals of two pair sums in every lane (the inclusive scan's lane
-// 63). Needs all 64 lanes active.
-__device__ __forceinline__ void wave_sum_sd(sd& a, sd& b) {
-  const uint32_t lane = threadIdx.x & 63u, rl = lane & 15u;
-  sd_scan_step<0x111>(a, b, rl >= 1u);  // row_shr:1
-  sd_scan_step<0x112>(a, b, rl >= 2u);  // row_shr:2
-  sd_scan_step<0x114>(a, b, rl >= 4u);  // row_shr:4
-  sd_scan_step<0x118>(a, b, rl >= 8u);  // row_shr:8
-  sd_scan_step<0x142>(a, b, (lane & 31u) >= 16u);  // row_bcast:15
-  sd_scan_step<0x143>(a, b, lane >= 32u);          // row_bcast:31
-  a = {readlane_f64(a.hi, 63), readlane_f64(a.lo, 63)};
-  b = {readlane_f64(b.hi, 63), readlane_f64(b.lo, 63)};
+// Totals over each row of 16 lanes, in every lane of the row: a butterfly of
+// lane swaps (quad_perm [1,0,3,2], [2,3,0,1], then the half-row and the row
+// mirrored), each step adding a lane's partner's partial. Needs all lanes
+// active.
+__device__ __forceinline__ void row_sum_moments(Moments& a) {
+  moments_step<0xb1>(a);   // quad_perm [1,0,3,2]
+  moments_step<0x4e>(a);   // quad_perm [2,3,0,1]
+  moments_step<0x141>(a);  // row_half_mirror
+  moments_step<0x140>(a);  // row_mirror
 }
 
-// Totals of two pair sums over lanes 0..15 (the first row's inclusive scan,
-// read back from lane 15 to every lane). Needs all 64 lanes active.
-__device__ __forceinline__ void row0_sum_sd(sd& a, sd& b) {
-  const uint32_t rl = threadIdx.x & 15u;
-  sd_scan_step<0x111>(a, b, rl >= 1u);  // row_shr:1
-  sd_scan_step<0x112>(a, b, rl >= 2u);  // row_shr:2
-  sd_scan_step<0x114>(a, b, rl >= 4u);  // row_shr:4
-  sd_scan_step<0x118>(a, b, rl >= 8u);  // row_shr:8
-  a = {readlane_f64(a.hi, 15), readlane_f64(a.lo, 15)};
-  b = {readlane_f64(b.hi, 15), readlane_f64(b.lo, 15)};
-}
-
-// Sums of a thread's E scores (keys) and of their squares. A power-of-two
-// offset sigma >= E * (largest score) goes in first: every running sum then
-// lies in [sigma, 2 sigma), at or above each addend, so Fast2Sum yields each
-// rounding error exactly, and taking sigma out at the end is exact
-// (Sterbenz). Squares of fp32 values are exact in fp64. Keys of 0 add
-// nothing.
+// log2 of the offsets for the largest key kmax: sigma1 >= E * (largest
+// score), sigma2 >= E * (its square).
 template <int E>
-__device__ __forceinline__ void thread_moments(const uint32_t (&key)[E], uint32_t kmax, sd& S1, sd& S2) {
+__device__ __forceinline__ void moments_log2_sigma(uint32_t kmax, int& l1, int& l2) {
   constexpr int LE = E <= 1 ? 0 : 32 - __builtin_clz((unsigned)(E - 1));  // ceil(log2 E)
   const int eb = max((int)(kmax >> 23), 1);  // largest score < 2^(eb - 126), its square < 2^(2 eb - 252)
-  const double sig1 = __longlong_as_double((long long)(eb - 126 + LE + 1023) << 52);
-  const double sig2 = __longlong_as_double((long long)(2 * eb - 252 + LE + 1023) << 52);
+  l1 = eb - 126 + LE;
+  l2 = 2 * eb - 252 + LE;
+}
+
+// A thread's share over its E keys (key e is input index(e); groups of four
+// that lie wholly past n in every lane of the wavefront are skipped: their
+// keys are 0). l1, l2: log2 of the workgroup's offsets.
+template <int E>
+__device__ __forceinline__ Moments thread_moments(const uint32_t (&key)[E], int l1, int l2, int n) {
+  const int t = threadIdx.x, w = t >> 6;
+  const double sig1 = __longlong_as_double((long long)(l1 + 1023) << 52);
+  const double sig2 = __longlong_as_double((long long)(l2 + 1023) << 52);
   double a1 = sig1, e1 = 0.0, a2 = sig2, e2 = 0.0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
+    if ((e & 3) == 0 && ((e >> 2) * GT + 64 * w) * 4 >= n) break;  // wavefront-uniform
     const double s = (double)__uint_as_float(key[e]);
     const double t1 = a1 + s;
     e1 += s - (t1 - a1);
@@ -265,8 +269,17 @@ __device__ __forceinline__ void thread_moments(const uint32_t (&key)[E], uint32_
     e2 += q - (t2 - a2);
     a2 = t2;
   }
-  S1 = {a1 - sig1, e1};
-  S2 = {a2 - sig2, e2};
+  constexpr uint64_t kMant = (1ull << 52) - 1ull;
+  return {(uint64_t)__double_as_longlong(a1) & kMant, (uint64_t)__double_as_longlong(a2) & kMant, e1, e2};
+}
+
+// i * 2^l + e as a double-double (i < 2^62 splits exactly into two doubles;
+// scaling by a power of two is exact).
+__device__ __forceinline__ dd moments_total(uint64_t i, double e, int l) {
+  const double sc = __longlong_as_double((long long)(l + 1023) << 52);
+  const double hi = (double)(uint32_t)(i >> 32) * 4294967296.0 * sc;
+  const double lo = (double)(uint32_t)i * sc;
+  return dd_add(two_sum(hi, lo), dd{e, 0.0});
 }
 
 // Threshold t (>= 0 keeps score > t; < 0 keeps everything) as a key pair.
@@ -322,7 +335,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
                                           uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
                                           double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
                                           uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
-                                          uint32_t* res, uint64_t* cand, sd (*dsum)[2],
+                                          uint32_t* res, uint64_t* cand, Moments* mrows,
                                           uint32_t (*kminmax)[2], int b, uint32_t& kthr_out,
                                           int& jlast_out) {
   SL_TL_DECL;
@@ -345,11 +358,23 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
   // same launch on other XCDs add onto the zeros). They are issued by
   // wavefronts w_lo.. while wavefront 0 works alone (bin search, final
   // scalar steps): issued beside the input loads they delayed those.
+  // The body goes out in 16-byte buffer stores with the same cache policy
+  // as a relaxed agent-scope atomic store (sc1): a quarter of the store
+  // instructions of a per-float clear; the unaligned head and the tail
+  // (< 4 floats each) take atomic stores.
   auto clear_y = [&](int w_lo) {
     if (zero_y != nullptr && w >= w_lo) {
       float* yb = zero_y + (size_t)b * m;
-      for (int i = t - 64 * w_lo; i < m; i += GT - 64 * w_lo)
-        __hip_atomic_store(yb + i, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int tt = t - 64 * w_lo, nt = GT - 64 * w_lo;
+      const int head = min(m, (int)((16u - ((uint32_t)(uintptr_t)yb & 15u)) & 15u) >> 2);
+      const int body = (m - head) >> 2;  // 16-byte groups
+      const int tail = m - head - 4 * body;
+      if (tt < head) __hip_atomic_store(yb + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tt < tail) __hip_atomic_store(yb + head + 4 * body + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(yb + head, 0, 16 * body, kRawBufferWord3);
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 z4 = {0u, 0u, 0u, 0u};
+      for (int i = tt; i < body; i += nt) __builtin_amdgcn_raw_buffer_store_b128(z4, r, 16 * i, 0, kPolicySc1);
     }
   };
 
@@ -504,47 +529,56 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
     }
   } else {
     if constexpr (MODE == MODE_STAT) {
-      sd S1{0.0, 0.0}, S2{0.0, 0.0};
-      uint32_t kmin = 0xffffffffu, kmax = 0u;
       const dd inv_n = dd_recip((double)n);  // early: its divisions stay off the final chain
-      {
-        // the token's scores: per-thread sums, per-wavefront totals, then
-        // the 16 wavefront totals in wavefront 0
-        uint32_t kall = 0u;
-        kmin = 0xffffffffu;
+      // the workgroup's largest and smallest score first (every thread's
+      // offset depends on the largest)
+      uint32_t kmax = 0u, kmin = 0xffffffffu;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          kall = max(kall, key[e]);  // padding keys are 0
-          if (index(e) < n) kmin = min(kmin, key[e]);
-        }
-        kmax = kall;
-        thread_moments<E>(key, kall, S1, S2);
-        wave_sum_sd(S1, S2);
-        kmax = wave_max(kmax);
-        kmin = ~wave_max(~kmin);
-        if (lane == 0) {
-          dsum[w][0] = S1;
-          dsum[w][1] = S2;
-          kminmax[w][0] = kmin;
-          kminmax[w][1] = kmax;
-        }
-        __syncthreads();
-        if (w == 0) {
-          S1 = lane < GW ? dsum[lane][0] : sd{0.0, 0.0};
-          S2 = lane < GW ? dsum[lane][1] : sd{0.0, 0.0};
-          kmin = lane < GW ? kminmax[lane][0] : 0xffffffffu;
-          kmax = lane < GW ? kminmax[lane][1] : 0u;
-        }
+      for (int e = 0; e < E; ++e) {
+        kmax = max(kmax, key[e]);  // padding keys are 0
+        if (index(e) < n) kmin = min(kmin, key[e]);
       }
+      kmax = wave_max(kmax);
+      kmin = ~wave_max(~kmin);
+      SL_TL(14);  // wavefront 0's keys are in
+      if (lane == 0) {
+        kminmax[w][0] = kmin;
+        kminmax[w][1] = kmax;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < GW; ++k) {
+        kmin = min(kmin, kminmax[k][0]);
+        kmax = max(kmax, kminmax[k][1]);
+      }
+      SL_TL(15);  // the workgroup's extremes known
+      int l1, l2;
+      moments_log2_sigma<E>(kmax, l1, l2);
+      Moments mt = thread_moments<E>(key, l1, l2, n);
+      row_sum_moments(mt);
+      SL_TL(16);  // wavefront 0's row totals
+      if ((lane & 15) == 0) mrows[4 * w + (lane >> 4)] = mt;
+      __syncthreads();
+      SL_TL(17);  // every row total in LDS
       clear_y(1);
       if (w == 0) {
-        // the wavefront totals sit in lanes 0..15 (nothing above)
-        row0_sum_sd(S1, S2);
-        kmax = wave_max(kmax);
-        kmin = ~wave_max(~kmin);
-        SL_TL(12);  // wavefront totals summed
+        // the 4 * GW row totals, one per lane: row sums again, then the four
+        // rows of this wavefront in a fixed order
+        static_assert(4 * GW == 64, "one row total per lane of wavefront 0");
+        mt = mrows[lane];
+        row_sum_moments(mt);
+        const uint64_t I1 = readlane_u64(mt.i1, 0) + readlane_u64(mt.i1, 16) + readlane_u64(mt.i1, 32) +
+                            readlane_u64(mt.i1, 48);
+        const uint64_t I2 = readlane_u64(mt.i2, 0) + readlane_u64(mt.i2, 16) + readlane_u64(mt.i2, 32) +
+                            readlane_u64(mt.i2, 48);
+        const double E1 = (readlane_f64(mt.e1, 0) + readlane_f64(mt.e1, 16)) +
+                          (readlane_f64(mt.e1, 32) + readlane_f64(mt.e1, 48));
+        const double E2 = (readlane_f64(mt.e2, 0) + readlane_f64(mt.e2, 16)) +
+                          (readlane_f64(mt.e2, 32) + readlane_f64(mt.e2, 48));
+        SL_TL(12);  // totals summed
         if (lane == 0) {
-          const dd T1 = fast_two_sum(S1.hi, S1.lo), T2 = fast_two_sum(S2.hi, S2.lo);
+          // sums = I * ulp(sigma) + E, ulp(sigma) = 2^(log2 sigma - 52)
+          const dd T1 = moments_total(I1, E1, l1 - 52), T2 = moments_total(I2, E2, l2 - 52);
           const dd mu = dd_mul(T1, inv_n);
           double var;
           double mean = mu.hi;
@@ -562,9 +596,11 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
           uint32_t kt;
           int jl;
           thresh_to_key(tt, n, kt, jl);
+          const uint64_t tb = (uint64_t)__double_as_longlong(tt);
           res[0] = kt;
           res[1] = (uint32_t)jl;
-          dsum[0][0].hi = tt;
+          res[2] = (uint32_t)tb;
+          res[3] = (uint32_t)(tb >> 32);
         }
         SL_TL(13);  // mu, sigma, t and the key pair computed
       }
@@ -572,7 +608,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       SL_TL(5);  // threshold known
       kthr = res[0];
       jlast = (int)res[1];
-      thresh = dsum[0][0].hi;
+      thresh = __longlong_as_double((long long)(((uint64_t)res[3] << 32) | res[2]));
     } else {  // MODE_FIXED
       clear_y(0);
       thresh = (double)tau;

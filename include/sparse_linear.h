@@ -271,11 +271,12 @@ sl_status sparse_linear_gather_ceiling(sl_handle h, const int32_t* idx, int32_t 
  * removes it (buf == NULL). While installed, every fused launch writes, for
  * workgroup b, the 100 MHz clock (s_memrealtime) at named points into word
  * 32 * b + slot: gate workgroup (b = 0): 0 start, 3 keys in, 7/8/9/10/11 the
- * top-K phases (first barrier, histogram, pivot bin, candidates, ranked),
- * 12 the wavefront totals of the moments summed, 13 mu, sigma and t
- * computed (one lane) and 5 threshold known (statistical gate), 6 selection
- * done, 1 pair published, 2 acknowledgements in; product workgroups: 0 start,
- * 23 moment part stored, 1 speculative list compacted (21: its length),
+ * top-K phases (first barrier, histogram, pivot bin, candidates, ranked);
+ * for the statistical gate 14 keys in, 15 largest and smallest score known,
+ * 16 row totals of the moment sums, 17 all row totals in LDS, 12 totals
+ * summed, 13 mu, sigma and t computed (one lane) and 5 threshold known; then 6 selection done, 1 pair
+ * published, 2 acknowledgements in; product workgroups: 0 start,
+ * 1 speculative list compacted (21: its length, held band included),
  * 2 early poll back (20: the value it read), 3 pair seen by the second poll,
  * 4 + w end of wavefront w's stream, 22 end. Only the timeline build of the
  * library (libsparse_linear_timeline.so) records anything; the regular
