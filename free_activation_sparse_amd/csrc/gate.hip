@@ -16,7 +16,7 @@ __global__ __launch_bounds__(GT) void gate_kernel(const XT* __restrict__ x, cons
                                                   double* __restrict__ thresh_out, float* __restrict__ zero_y,
                                                   int m, int vec) {
   __shared__ __align__(16) uint32_t h1[MODE == MODE_TOPK ? 4096 : 1];
-  __shared__ uint32_t h2[MODE == MODE_TOPK ? 4096 : 1];
+  __shared__ __align__(16) uint32_t h2[MODE == MODE_TOPK ? 4096 : 1];
   __shared__ uint32_t h3[MODE == MODE_TOPK ? 128 : 1];
   __shared__ uint64_t cand[MODE == MODE_TOPK ? 64 : 1];
   __shared__ uint32_t wsum[GW];

@@ -3,6 +3,11 @@
 //
 //  * Top-K (WINA article, section 一): selection on the scores' fp32 bit
 //    patterns (non-negative, so unsigned order is numeric order).
+//    Window path (a previous call on this slot left its K-th key): one pass
+//    counts the keys above a window around that key and histograms the
+//    window's keys into 1024 LDS bins; one wavefront finds the bin holding
+//    rank K, whose keys (at most 64) are ranked exactly. Otherwise, or when
+//    rank K falls outside the window or in a bin of more than 64 keys:
 //    Fast path: a 4096-bin LDS histogram of key>>14 over the eight binades
 //    below the largest key (512 bins per binade: few atomic collisions),
 //    searched by one wavefront; the pivot bin's keys (at most 64) are
@@ -13,9 +18,8 @@
 //    kept ties' last index by a radix select on the index (8/7 bits).
 //  * Statistical threshold (Spark Transformer article, section 2.2): mean and
 //    population variance of the scores from double-double sums, each rounded
-//    once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)). The sums
-//    come from this workgroup's own scores, or (fused forward) from partial
-//    sums of 64-input slices that the product workgroups publish.
+//    once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)), from the
+//    workgroup's own scores.
 //  * Fixed threshold: kthr from the per-layer tau (WINA article, section 三,
 //    calibrated per-layer thresholds).
 //
@@ -40,6 +44,11 @@ using namespace sl::dev;
 constexpr int GT = 1024;      // threads per gate workgroup
 constexpr int GW = GT / 64;   // wavefronts per gate workgroup
 constexpr int MODE_TOPK = 0, MODE_STAT = 1, MODE_FIXED = 2;
+
+// Top-K window select around the previous K-th key (see gate_select): the
+// window's edges over the previous K-th score, and its histogram bins.
+constexpr float kWinLow = 0.87f, kWinHigh = 1.15f;
+constexpr int kWinBins = 1024;
 
 // ---------------------------------------------------------------- scans
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum) {
@@ -294,6 +303,24 @@ __device__ __forceinline__ void thresh_to_key(double t, int n, uint32_t& kthr, i
   }
 }
 
+// ---------------------------------------------------------------- clearing
+// Zeroes y[0 .. m) from threads tt = 0 .. nt - 1 with device-coherent stores
+// (product workgroups on other XCDs add onto the zeros): the body in 16-byte
+// buffer stores with the same cache policy as a relaxed agent-scope atomic
+// store (sc1), a quarter of the store instructions of a per-float clear; the
+// unaligned head and the tail (< 4 floats each) take atomic stores.
+__device__ __forceinline__ void clear_coherent(float* yb, int m, int tt, int nt) {
+  const int head = min(m, (int)((16u - ((uint32_t)(uintptr_t)yb & 15u)) & 15u) >> 2);
+  const int body = (m - head) >> 2;  // 16-byte groups
+  const int tail = m - head - 4 * body;
+  if (tt < head) __hip_atomic_store(yb + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tt < tail) __hip_atomic_store(yb + head + 4 * body + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(yb + head, 0, 16 * body, kRawBufferWord3);
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  for (int i = tt; i < body; i += nt) __builtin_amdgcn_raw_buffer_store_b128(z4, r, 16 * i, 0, kPolicySc1);
+}
+
 // ---------------------------------------------------------------- loads
 // Keys of group g (4 inputs starting at 4 * (g * GT + t)); out-of-range
 // inputs get key 0 and must be masked by the caller with their index.
@@ -329,22 +356,35 @@ __device__ __forceinline__ void load_group(const XT* __restrict__ xb, const floa
   for (int e = 0; e < 4; ++e) k[e] = (base + e < n) ? score_key(xv[e], cv[e]) : 0u;
 }
 
-template <typename XT, int G, int MODE, bool VEC>
-__device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float* __restrict__ c, int n, int K,
-                                          double z, float tau, sl::GateOut* __restrict__ gout,
-                                          uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
-                                          double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
-                                          uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
-                                          uint32_t* res, uint64_t* cand, Moments* mrows,
-                                          uint32_t (*kminmax)[2], int b, uint32_t& kthr_out,
-                                          int& jlast_out) {
-  SL_TL_DECL;
-  constexpr int E = 4 * G;
-  const int t = threadIdx.x, lane = t & 63, w = wave_id();
-  const XT* xb = x + (size_t)b * n;
-  auto index = [&](int e) { return ((e >> 2) * GT + t) * 4 + (e & 3); };
+// Top-K: the previous call's K-th key for this slot (the prior of the window
+// select in gate_select; any value is safe, it only picks the path), and that
+// select's histogram (h2) and counters cleared before its keys are used. Ends
+// with a barrier when it clears them.
+template <int MODE>
+__device__ __forceinline__ uint32_t gate_prologue(int K, const sl::GateOut* gout, int b, uint32_t* h2,
+                                                  uint32_t* res) {
+  uint32_t prevk = 0u;
+  if constexpr (MODE == MODE_TOPK) {
+    if (K > 0) {
+      const int t = threadIdx.x;
+      prevk = gout[b].kthr;
+      for (int i = t; i < kWinBins; i += GT) h2[i] = 0u;
+      if (t == 0) {
+        res[0] = 0xffffffffu;
+        res[3] = 0u;
+      }
+      __syncthreads();
+    }
+  }
+  return prevk;
+}
 
-  uint32_t key[E];
+// The scores' keys of token b: thread t holds groups t, t + GT, ... of 4
+// consecutive inputs (key[4 g + e] is input 4 (g GT + t) + e); 0 past n.
+template <typename XT, int G, bool VEC>
+__device__ __forceinline__ void gate_keys(const XT* __restrict__ x, const float* __restrict__ c, int n, int b,
+                                          uint32_t (&key)[4 * G]) {
+  const XT* xb = x + (size_t)b * n;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     uint32_t k4[4];
@@ -352,30 +392,30 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
 #pragma unroll
     for (int e = 0; e < 4; ++e) key[g * 4 + e] = k4[e];
   }
+}
+
+// The selection on keys from gate_keys, with prevk from gate_prologue (which
+// must have run, in every thread, before it); outputs as gate_body.
+template <int G, int MODE>
+__device__ __forceinline__ void gate_select(const uint32_t (&key)[4 * G], uint32_t prevk, int n, int K, double z,
+                                            float tau, sl::GateOut* __restrict__ gout,
+                                            uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
+                                            double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
+                                            uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
+                                            uint32_t* res, uint64_t* cand, Moments* mrows,
+                                            uint32_t (*kminmax)[2], int b, uint32_t& kthr_out, int& jlast_out) {
+  SL_TL_DECL;
+  constexpr int E = 4 * G;
+  const int t = threadIdx.x, lane = t & 63, w = wave_id();
+  auto index = [&](int e) { return ((e >> 2) * GT + t) * 4 + (e & 3); };
 
   // The product that follows adds its split partials into y atomically, so
   // y is cleared here with device-coherent stores (product workgroups of the
   // same launch on other XCDs add onto the zeros). They are issued by
   // wavefronts w_lo.. while wavefront 0 works alone (bin search, final
   // scalar steps): issued beside the input loads they delayed those.
-  // The body goes out in 16-byte buffer stores with the same cache policy
-  // as a relaxed agent-scope atomic store (sc1): a quarter of the store
-  // instructions of a per-float clear; the unaligned head and the tail
-  // (< 4 floats each) take atomic stores.
   auto clear_y = [&](int w_lo) {
-    if (zero_y != nullptr && w >= w_lo) {
-      float* yb = zero_y + (size_t)b * m;
-      const int tt = t - 64 * w_lo, nt = GT - 64 * w_lo;
-      const int head = min(m, (int)((16u - ((uint32_t)(uintptr_t)yb & 15u)) & 15u) >> 2);
-      const int body = (m - head) >> 2;  // 16-byte groups
-      const int tail = m - head - 4 * body;
-      if (tt < head) __hip_atomic_store(yb + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (tt < tail) __hip_atomic_store(yb + head + 4 * body + tt, 0.f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(yb + head, 0, 16 * body, kRawBufferWord3);
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 z4 = {0u, 0u, 0u, 0u};
-      for (int i = tt; i < body; i += nt) __builtin_amdgcn_raw_buffer_store_b128(z4, r, 16 * i, 0, kPolicySc1);
-    }
+    if (zero_y != nullptr && w >= w_lo) clear_coherent(zero_y + (size_t)b * m, m, t - 64 * w_lo, GT - 64 * w_lo);
   };
 
   uint32_t kthr = 0xffffffffu;
@@ -389,6 +429,112 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       clear_y(0);
       thresh = __longlong_as_double(0x7ff0000000000000ll);  // +inf: nothing kept
     } else {
+      // The r-th (1-based) largest of the c1 <= 64 keys for which in_bin
+      // holds, under (score descending, index ascending), into res[1] (key)
+      // and res[2] (index): the keys are compacted as (key, ~index)
+      // composites (larger composite = earlier in the order; composites are
+      // distinct) with one LDS atomic per wavefront reserving its slots
+      // (res[3] must be 0), then wavefront 0 ranks them, lane a comparing
+      // candidate a with every other through readlane.
+      auto rank_bin = [&](auto in_bin, uint32_t c1, uint32_t r) {
+        uint64_t bal[E];
+        uint32_t wtot = 0u;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          bal[e] = __ballot(in_bin(key[e]));
+          wtot += (uint32_t)__popcll(bal[e]);
+        }
+        if (wtot != 0u) {
+          uint32_t off = 0u;
+          if (lane == 0) off = atomicAdd(&res[3], wtot);
+          off = (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            if (bal[e] != 0ull) {  // uniform: most slots hold no candidate
+              if ((bal[e] >> lane) & 1ull)
+                cand[off + lanes_below(bal[e])] = ((uint64_t)key[e] << 32) | (uint64_t)(~(uint32_t)index(e));
+              off += (uint32_t)__popcll(bal[e]);
+            }
+          }
+        }
+        __syncthreads();
+        SL_TL(10);
+        if (w == 0) {
+          const uint64_t ca = (uint32_t)lane < c1 ? cand[lane] : 0ull;
+          const uint32_t chi = (uint32_t)(ca >> 32), clo = (uint32_t)ca;
+          uint32_t above = 0u;
+          for (int k = 0; k < (int)c1; ++k) {
+            const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)chi, k) << 32) |
+                               (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)clo, k);
+            above += (o > ca) ? 1u : 0u;
+          }
+          if ((uint32_t)lane < c1 && above == r - 1u) {
+            res[1] = chi;
+            res[2] = ~clo;
+          }
+        }
+        __syncthreads();
+        SL_TL(11);
+      };
+
+      // Window select around the prior: consecutive tokens' K-th scores
+      // differ by a few percent, so the K-th key almost always lies in
+      // [lo, hi) = [kWinLow, kWinHigh) times the previous one. One pass
+      // counts the keys at or above hi (ballots) and histograms the keys in
+      // the window into kWinBins bins (LDS atomics: only the window's keys,
+      // a fraction of n); one wavefront finds the bin holding rank K, and
+      // its keys are ranked exactly. No maximum, no full-range histogram.
+      // Falls through to the full select when the K-th key lies outside the
+      // window or its bin holds more than 64 keys (heavy ties). (Keeping
+      // each bin's largest and smallest composite as well, to skip the
+      // ranking when rank K is a bin's first or last entry, cost more in
+      // 64-bit LDS atomics than the ranking it saved.)
+      bool found = false;
+      if (prevk != 0u && prevk < 0x7f800000u) {  // uniform
+        const float pf = __uint_as_float(prevk);
+        uint32_t hi = __float_as_uint(pf * kWinHigh), lo = __float_as_uint(pf * kWinLow);
+        if (hi <= prevk) hi = prevk + 1u;
+        if (lo > prevk) lo = prevk;
+        if (lo == 0u) lo = 1u;  // padding keys (0) never enter the window
+        const uint32_t span = hi - lo;
+        const int sh = max(0, 22 - (int)__builtin_clz((span - 1u) | 1u));  // (span - 1) >> sh < kWinBins
+        static_assert(kWinBins == 1024, "window shift assumes 1024 bins");
+        uint32_t ws = 0u;
+        SL_TL(3);  // wavefront 0's keys are in (their first use follows)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          ws += (uint32_t)__popcll(__ballot(key[e] >= hi));
+          const uint32_t d = key[e] - lo;  // wraps above span below the window
+          if (d < span) atomicAdd(&h2[d >> sh], 1u);
+        }
+        if (lane == 0) wsum[w] = ws;
+        __syncthreads();
+        SL_TL(18);
+        uint32_t above_hi = 0u;
+#pragma unroll
+        for (int k = 0; k < GW; ++k) above_hi += wsum[k];
+        // (res[0] stays "not found" unless the window holds rank K)
+        if (above_hi < (uint32_t)K) {  // uniform
+          if (w == 0)
+            find_bin_wave<kWinBins, 8>(h2, (uint32_t)K - above_hi, res);
+          else
+            clear_y(1);
+        }
+        // every wavefront has read wsum and res[0..2] is final before either
+        // path below writes them
+        __syncthreads();
+        SL_TL(19);
+        const uint32_t b1 = res[0], c1 = res[2];
+        if (b1 != 0xffffffffu && c1 <= 64u) {  // uniform
+          const uint32_t r1 = (uint32_t)K - above_hi - res[1];  // rank inside the bin, 1-based
+          rank_bin([&](uint32_t k) { return k - lo < span && ((k - lo) >> sh) == b1; }, c1, r1);
+          kthr = res[1];
+          jlast = (int)res[2];
+          found = true;
+        }
+      }
+
+      if (!found) {
       for (int i = t; i < 4096; i += GT) h1[i] = 0u;
       uint32_t lmax = 0u;
 #pragma unroll
@@ -429,47 +575,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
       if (in_window && c1 <= 64u) {
         const uint32_t b1 = res[0] + base;         // pivot bin of key>>14 (>= 1: never a padding key's)
         const uint32_t r1 = (uint32_t)K - res[1];  // rank wanted inside the pivot bin, 1-based
-        // candidates as (key, ~index): larger composite = earlier in the order
-        // (score descending, index ascending); composites are distinct. One
-        // LDS atomic per wavefront reserves its slots.
-        uint64_t bal[E];
-        uint32_t wtot = 0u;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          bal[e] = __ballot((key[e] >> 14) == b1);
-          wtot += (uint32_t)__popcll(bal[e]);
-        }
-        if (wtot != 0u) {
-          uint32_t off = 0u;
-          if (lane == 0) off = atomicAdd(&res[3], wtot);
-          off = (uint32_t)__builtin_amdgcn_readfirstlane((int)off);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            if ((bal[e] >> lane) & 1ull)
-              cand[off + lanes_below(bal[e])] = ((uint64_t)key[e] << 32) | (uint64_t)(~(uint32_t)index(e));
-            off += (uint32_t)__popcll(bal[e]);
-          }
-        }
-        __syncthreads();
-        SL_TL(10);
-        // rank of each candidate among the c1, by wavefront 0 (lane a holds
-        // candidate a and compares it with every other through readlane)
-        if (w == 0) {
-          const uint64_t ca = (uint32_t)lane < c1 ? cand[lane] : 0ull;
-          const uint32_t chi = (uint32_t)(ca >> 32), clo = (uint32_t)ca;
-          uint32_t above = 0u;
-          for (int k = 0; k < (int)c1; ++k) {
-            const uint64_t o = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)chi, k) << 32) |
-                               (uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)clo, k);
-            above += (o > ca) ? 1u : 0u;
-          }
-          if ((uint32_t)lane < c1 && above == r1 - 1u) {
-            res[1] = chi;
-            res[2] = ~clo;
-          }
-        }
-        __syncthreads();
-        SL_TL(11);
+        rank_bin([&](uint32_t k) { return (k >> 14) == b1; }, c1, r1);
         kthr = res[1];
         jlast = (int)res[2];
       } else {
@@ -525,6 +631,7 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
         kthr = vstar;
         jlast = (int)((hiidx << 7) | (127u - res[0]));
       }
+      }  // !found
       thresh = (double)__uint_as_float(kthr);
     }
   } else {
@@ -647,6 +754,24 @@ __device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float*
   SL_TL(6);
   kthr_out = kthr;
   jlast_out = jlast;
+}
+
+// One token's gate: keys, then the selection (prologue first, so that the
+// select's histogram is cleared while the loads are in flight).
+template <typename XT, int G, int MODE, bool VEC>
+__device__ __forceinline__ void gate_body(const XT* __restrict__ x, const float* __restrict__ c, int n, int K,
+                                          double z, float tau, sl::GateOut* __restrict__ gout,
+                                          uint8_t* __restrict__ mask_out, int32_t* __restrict__ count_out,
+                                          double* __restrict__ thresh_out, float* __restrict__ zero_y, int m,
+                                          uint32_t* h1, uint32_t* h2, uint32_t* h3, uint32_t* wsum,
+                                          uint32_t* res, uint64_t* cand, Moments* mrows,
+                                          uint32_t (*kminmax)[2], int b, uint32_t& kthr_out,
+                                          int& jlast_out) {
+  const uint32_t prevk = gate_prologue<MODE>(K, gout, b, h2, res);
+  uint32_t key[4 * G];
+  gate_keys<XT, G, VEC>(x, c, n, b, key);
+  gate_select<G, MODE>(key, prevk, n, K, z, tau, gout, mask_out, count_out, thresh_out, zero_y, m, h1, h2, h3,
+                       wsum, res, cand, mrows, kminmax, b, kthr_out, jlast_out);
 }
 
 }  // namespace gatedev
