@@ -783,7 +783,7 @@ def run_ds_decode(args):
 
 # Slots of the fused forward's timestamps (sparse_linear_set_timeline).
 TL_GATE = {"keys": 3, "window_counted": 18, "window_pivot": 19, "first_barrier": 7, "histogram": 8, "pivot_bin": 9, "candidates": 10, "ranked": 11,
-           "stat_keys": 14, "extremes": 15, "row_totals": 16, "totals_in_lds": 17,
+           "stat_keys": 14, "extremes_and_plain_sums": 15, "first_threshold_checked": 16, "totals_in_lds": 17,
            "totals_summed": 12, "threshold_computed": 13, "threshold": 5, "selected": 6,
            "published": 1, "acks_in": 2}
 TL_PROD = {"compacted": 1, "early_poll_back": 2, "pair_polled": 3, "end": 22}

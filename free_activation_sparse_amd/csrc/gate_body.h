@@ -17,9 +17,13 @@
 //    bin, i.e. heavy ties): radix select on 12/12/7-bit key digits, then the
 //    kept ties' last index by a radix select on the index (8/7 bits).
 //  * Statistical threshold (Spark Transformer article, section 2.2): mean and
-//    population variance of the scores from double-double sums, each rounded
-//    once to fp64; sigma by IEEE sqrt; t = fl(mu + fl(sigma * z)), from the
-//    workgroup's own scores.
+//    population variance of the scores, each rounded once to fp64; sigma by
+//    IEEE sqrt; t = fl(mu + fl(sigma * z)), from the workgroup's own scores.
+//    A first threshold from plain fp64 sums comes with a rigorous bound on
+//    its distance from the exact t; when no score lies within that bound
+//    (almost always) it decides the kept set, and the exact moments (sums
+//    in double-double) are only computed for the threshold output or when a
+//    score is that close.
 //  * Fixed threshold: kthr from the per-layer tau (WINA article, section 三,
 //    calibrated per-layer thresholds).
 //
@@ -247,6 +251,19 @@ __device__ __forceinline__ void row_sum_moments(Moments& a) {
   moments_step<0x140>(a);  // row_mirror
 }
 
+// Totals of two doubles over each row of 16 lanes, in every lane of the row
+// (the butterfly of row_sum_moments). Needs all lanes active.
+__device__ __forceinline__ void row_sum2(double& a, double& b) {
+  a += dpp_f64<0xb1>(a);
+  b += dpp_f64<0xb1>(b);
+  a += dpp_f64<0x4e>(a);
+  b += dpp_f64<0x4e>(b);
+  a += dpp_f64<0x141>(a);
+  b += dpp_f64<0x141>(b);
+  a += dpp_f64<0x140>(a);
+  b += dpp_f64<0x140>(b);
+}
+
 // log2 of the offsets for the largest key kmax: sigma1 >= E * (largest
 // score), sigma2 >= E * (its square).
 template <int E>
@@ -413,7 +430,9 @@ __device__ __forceinline__ void gate_select(const uint32_t (&key)[4 * G], uint32
   // y is cleared here with device-coherent stores (product workgroups of the
   // same launch on other XCDs add onto the zeros). They are issued by
   // wavefronts w_lo.. while wavefront 0 works alone (bin search, final
-  // scalar steps): issued beside the input loads they delayed those.
+  // scalar steps): issued right behind the input loads, even as a fixed
+  // number of stores per thread, they delayed the keys by ~0.4 us and the
+  // top-K selection by ~0.9 us.
   auto clear_y = [&](int w_lo) {
     if (zero_y != nullptr && w >= w_lo) clear_coherent(zero_y + (size_t)b * m, m, t - 64 * w_lo, GT - 64 * w_lo);
   };
@@ -637,20 +656,31 @@ __device__ __forceinline__ void gate_select(const uint32_t (&key)[4 * G], uint32
   } else {
     if constexpr (MODE == MODE_STAT) {
       const dd inv_n = dd_recip((double)n);  // early: its divisions stay off the final chain
-      // the workgroup's largest and smallest score first (every thread's
-      // offset depends on the largest)
+      // One pass over the keys: the workgroup's extremes and plain fp64 sums
+      // of s and s^2 (groups of four wholly past n are skipped: their keys
+      // are 0).
       uint32_t kmax = 0u, kmin = 0xffffffffu;
+      double f1 = 0.0, f2 = 0.0;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
+        if ((e & 3) == 0 && ((e >> 2) * GT + 64 * w) * 4 >= n) break;  // wavefront-uniform
         kmax = max(kmax, key[e]);  // padding keys are 0
         if (index(e) < n) kmin = min(kmin, key[e]);
+        const double sv = (double)__uint_as_float(key[e]);
+        f1 += sv;
+        f2 += sv * sv;
       }
       kmax = wave_max(kmax);
       kmin = ~wave_max(~kmin);
       SL_TL(14);  // wavefront 0's keys are in
+      row_sum2(f1, f2);
       if (lane == 0) {
         kminmax[w][0] = kmin;
         kminmax[w][1] = kmax;
+      }
+      if ((lane & 15) == 0) {
+        mrows[4 * w + (lane >> 4)].e1 = f1;
+        mrows[4 * w + (lane >> 4)].e2 = f2;
       }
       __syncthreads();
 #pragma unroll
@@ -658,64 +688,130 @@ __device__ __forceinline__ void gate_select(const uint32_t (&key)[4 * G], uint32
         kmin = min(kmin, kminmax[k][0]);
         kmax = max(kmax, kminmax[k][1]);
       }
-      SL_TL(15);  // the workgroup's extremes known
-      int l1, l2;
-      moments_log2_sigma<E>(kmax, l1, l2);
-      Moments mt = thread_moments<E>(key, l1, l2, n);
-      row_sum_moments(mt);
-      SL_TL(16);  // wavefront 0's row totals
-      if ((lane & 15) == 0) mrows[4 * w + (lane >> 4)] = mt;
-      __syncthreads();
-      SL_TL(17);  // every row total in LDS
+      SL_TL(15);  // the workgroup's extremes and the plain sums' row totals known
+      // A first threshold from the plain sums, with a rigorous bound on its
+      // distance from the exact one: every sum adds non-negative terms, so
+      // each total is within (n - 1) u <= 2^-38 (relative) of the exact sum
+      // whatever the order; mu within 2^-36, E[s^2] - mu^2 within 2^-34 E[s^2],
+      // sigma within 2^-34 E[s^2] / sigma, and t within
+      // del = 2^-32 (mu + |z| sigma + |z| E[s^2] / sigma), a margin of 4 or
+      // more over each term (the roundings of the exact t itself included).
+      // If no score lies within del of this t, every score compares with
+      // it as with the exact t, and the kept set is final; otherwise, for
+      // near-constant scores, or when t is not safely positive, the exact
+      // moments decide (below).
       clear_y(1);
       if (w == 0) {
-        // the 4 * GW row totals, one per lane: row sums again, then the four
-        // rows of this wavefront in a fixed order
         static_assert(4 * GW == 64, "one row total per lane of wavefront 0");
-        mt = mrows[lane];
-        row_sum_moments(mt);
-        const uint64_t I1 = readlane_u64(mt.i1, 0) + readlane_u64(mt.i1, 16) + readlane_u64(mt.i1, 32) +
-                            readlane_u64(mt.i1, 48);
-        const uint64_t I2 = readlane_u64(mt.i2, 0) + readlane_u64(mt.i2, 16) + readlane_u64(mt.i2, 32) +
-                            readlane_u64(mt.i2, 48);
-        const double E1 = (readlane_f64(mt.e1, 0) + readlane_f64(mt.e1, 16)) +
-                          (readlane_f64(mt.e1, 32) + readlane_f64(mt.e1, 48));
-        const double E2 = (readlane_f64(mt.e2, 0) + readlane_f64(mt.e2, 16)) +
-                          (readlane_f64(mt.e2, 32) + readlane_f64(mt.e2, 48));
-        SL_TL(12);  // totals summed
+        double g1 = mrows[lane].e1, g2 = mrows[lane].e2;
+        row_sum2(g1, g2);
+        const double F1 = (readlane_f64(g1, 0) + readlane_f64(g1, 16)) + (readlane_f64(g1, 32) + readlane_f64(g1, 48));
+        const double F2 = (readlane_f64(g2, 0) + readlane_f64(g2, 16)) + (readlane_f64(g2, 32) + readlane_f64(g2, 48));
         if (lane == 0) {
-          // sums = I * ulp(sigma) + E, ulp(sigma) = 2^(log2 sigma - 52)
-          const dd T1 = moments_total(I1, E1, l1 - 52), T2 = moments_total(I2, E2, l2 - 52);
-          const dd mu = dd_mul(T1, inv_n);
-          double var;
-          double mean = mu.hi;
-          if (kmin == kmax) {  // all scores equal: exact mean, zero variance
-            mean = (double)__uint_as_float(kmin);
-            var = 0.0;
-          } else {
-            const dd ex2 = dd_mul(T2, inv_n);
-            const dd msq = dd_sqr(mu);
-            const dd v = dd_add(ex2, dd{-msq.hi, -msq.lo});
-            var = v.hi > 0.0 ? v.hi : 0.0;
-          }
-          const double sigma = sqrt(var);
-          const double tt = __dadd_rn(mean, __dmul_rn(sigma, z));
-          uint32_t kt;
-          int jl;
-          thresh_to_key(tt, n, kt, jl);
-          const uint64_t tb = (uint64_t)__double_as_longlong(tt);
-          res[0] = kt;
-          res[1] = (uint32_t)jl;
-          res[2] = (uint32_t)tb;
-          res[3] = (uint32_t)(tb >> 32);
+          const double mu = F1 * inv_n.hi, e2 = F2 * inv_n.hi;
+          const double v = e2 - mu * mu;
+          uint32_t ok = (kmin != kmax && v > 0x1p-20 * e2) ? 1u : 0u;
+          const double sg = ok ? sqrt(v) : 1.0;
+          const double t0 = mu + sg * z;
+          const double az = fabs(z);
+          const double del = 0x1p-32 * (mu + az * sg + az * (e2 / sg));
+          const double lo = t0 - del, hi = t0 + del;
+          if (!(lo > 0.0)) ok = 0u;
+          res[0] = __float_as_uint(__double2float_rd(lo));
+          res[1] = __float_as_uint(__double2float_ru(hi));
+          res[2] = __float_as_uint(__double2float_rz(t0)) & 0x7fffffffu;
+          res[3] = ok;
+          cand[0] = (uint64_t)__double_as_longlong(t0);
         }
-        SL_TL(13);  // mu, sigma, t and the key pair computed
       }
       __syncthreads();
-      SL_TL(5);  // threshold known
-      kthr = res[0];
-      jlast = (int)res[1];
-      thresh = __longlong_as_double((long long)(((uint64_t)res[3] << 32) | res[2]));
+      const uint32_t klo = res[0], kspan = res[1] - res[0], kfast = res[2];
+      const double tfast = __longlong_as_double((long long)cand[0]);
+      bool fast = false;
+      if (res[3] != 0u) {  // uniform
+        bool amb = false;
+#pragma unroll
+        for (int e = 0; e < E; ++e) amb |= key[e] - klo <= kspan;  // (padding keys 0 lie below klo > 0)
+        // per-wavefront flags in kminmax (read for the last time before the
+        // barrier above; wsum is the count's, written without a barrier)
+        const uint64_t ab = __ballot(amb);
+        if (lane == 0) kminmax[w][0] = ab != 0ull ? 1u : 0u;
+        __syncthreads();
+        uint32_t anyamb = 0u;
+#pragma unroll
+        for (int k = 0; k < GW; ++k) anyamb |= kminmax[k][0];
+        fast = anyamb == 0u;
+      }
+      SL_TL(16);  // the first threshold checked
+      if (fast) {
+        kthr = kfast;  // keys > kfast  <=>  score > t (no score within del of either)
+        jlast = -1;
+        thresh = tfast;
+      }
+      if (!fast || thresh_out != nullptr) {  // uniform
+        // Exact moments: sums of s and s^2 to ~2^-100 relative, far below the
+        // single rounding to fp64 that the mean and the variance take. Every
+        // thread adds its E scores onto a power-of-two offset sigma >= E *
+        // (the workgroup's largest score), the same for all threads (see
+        // thread_moments); the running sums' mantissa fields add exactly in
+        // uint64, and only the tiny error sums round.
+        int l1, l2;
+        moments_log2_sigma<E>(kmax, l1, l2);
+        Moments mt = thread_moments<E>(key, l1, l2, n);
+        row_sum_moments(mt);
+        if ((lane & 15) == 0) mrows[4 * w + (lane >> 4)] = mt;
+        __syncthreads();
+        SL_TL(17);  // every row total in LDS
+        if (w == 0) {
+          // the 4 * GW row totals, one per lane: row sums again, then the four
+          // rows of this wavefront in a fixed order
+          mt = mrows[lane];
+          row_sum_moments(mt);
+          const uint64_t I1 = readlane_u64(mt.i1, 0) + readlane_u64(mt.i1, 16) + readlane_u64(mt.i1, 32) +
+                              readlane_u64(mt.i1, 48);
+          const uint64_t I2 = readlane_u64(mt.i2, 0) + readlane_u64(mt.i2, 16) + readlane_u64(mt.i2, 32) +
+                              readlane_u64(mt.i2, 48);
+          const double E1 = (readlane_f64(mt.e1, 0) + readlane_f64(mt.e1, 16)) +
+                            (readlane_f64(mt.e1, 32) + readlane_f64(mt.e1, 48));
+          const double E2 = (readlane_f64(mt.e2, 0) + readlane_f64(mt.e2, 16)) +
+                            (readlane_f64(mt.e2, 32) + readlane_f64(mt.e2, 48));
+          SL_TL(12);  // totals summed
+          if (lane == 0) {
+            // sums = I * ulp(sigma) + E, ulp(sigma) = 2^(log2 sigma - 52)
+            const dd T1 = moments_total(I1, E1, l1 - 52), T2 = moments_total(I2, E2, l2 - 52);
+            const dd mu = dd_mul(T1, inv_n);
+            double var;
+            double mean = mu.hi;
+            if (kmin == kmax) {  // all scores equal: exact mean, zero variance
+              mean = (double)__uint_as_float(kmin);
+              var = 0.0;
+            } else {
+              const dd ex2 = dd_mul(T2, inv_n);
+              const dd msq = dd_sqr(mu);
+              const dd v = dd_add(ex2, dd{-msq.hi, -msq.lo});
+              var = v.hi > 0.0 ? v.hi : 0.0;
+            }
+            const double sigma = sqrt(var);
+            const double tt = __dadd_rn(mean, __dmul_rn(sigma, z));
+            uint32_t kt;
+            int jl;
+            thresh_to_key(tt, n, kt, jl);
+            const uint64_t tb = (uint64_t)__double_as_longlong(tt);
+            res[0] = kt;
+            res[1] = (uint32_t)jl;
+            res[2] = (uint32_t)tb;
+            res[3] = (uint32_t)(tb >> 32);
+          }
+          SL_TL(13);  // mu, sigma, t and the key pair computed
+        }
+        __syncthreads();
+        SL_TL(5);  // exact threshold known
+        if (!fast) {
+          kthr = res[0];
+          jlast = (int)res[1];
+        }
+        thresh = __longlong_as_double((long long)(((uint64_t)res[3] << 32) | res[2]));
+      }
     } else {  // MODE_FIXED
       clear_y(0);
       thresh = (double)tau;
