@@ -801,8 +801,8 @@ def timeline_summary(launches):
     hits, nwg = [], []
     for a in launches:
         a = a.astype(np.int64)
-        n = int((a[:, 0] != 0).sum())
-        a = a[:n]
+        a = a[a[:, 0] != 0]  # workgroups that record (the gate first; clearing workgroups record nothing)
+        n = a.shape[0]
         base = a[:, 0].min()
         us = lambda v: (v - base) * 0.01  # s_memrealtime: 100 MHz
         for k, slot in TL_GATE.items():

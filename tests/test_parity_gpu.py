@@ -183,6 +183,30 @@ def test_stat_gate_constant_scores(fas, dtype, fused):
     assert torch.count_nonzero(out["y"]).item() == 0
 
 
+@pytest.mark.parametrize("p,s_keep", [(0.5, 0.15865525393145707), (0.2, 0.02275013194817921)])
+@pytest.mark.parametrize("fused", [True, False])
+def test_stat_threshold_on_a_score(fas, p, s_keep, fused):
+    """Two score values a > b, a fraction p of the inputs at a, and s_keep =
+    1 - Phi(sqrt((1 - p) / p)): then t = a up to the last bits of z, so a
+    score lies within any rounding bound of t. The first threshold from plain
+    sums cannot decide such a token; the exact moments must, bit for bit (all
+    inputs at a kept or none, as the exact t falls)."""
+    m, n = 1024, 6000
+    W = wl.random_matrix(140, m, n, "bf16")
+    c = np.ones(n, np.float32)
+    layer = _layer(fas, W, c, "stat", s_keep=s_keep)
+    layer.set_fused(fused)
+    rng = np.random.default_rng(141)
+    for t in range(3):
+        x = np.ones(n, np.float32)
+        x[rng.permutation(n)[: int(round(p * n))]] = 2.0
+        x *= np.float32(1.0 + 0.25 * t)  # a, b exact in bf16
+        xb = wl.f32_to_bf16_bits(x)
+        out = _fwd(layer, xb)
+        check_token(out, 0, W, c, xb, "stat", s_keep=s_keep, ctx=f"stat on a score p={p} token {t}")
+    layer.close()
+
+
 def test_stat_fused_plans(fas):
     """Fused statistical gate under every launch shape (row tiles of 128, 256
     and 512 rows; 1 to 150 input chunks, including more workgroups than the
