@@ -443,13 +443,20 @@ def workload_legs(name):
         return [("grouped", 1, lins, groups), ("block", 1, lins, None)]
     if name == "phi4_ffn_stat":
         lins = [(4, li, dict(gate="stat", s_keep=0.10)) for li in range(3)]
-        # "B1_grouped": gate and up in one launch (gate's token for both), then down
-        return [("B1_grouped", 1, lins, [[0, 1], [2]])] + [(f"B{b}", b, lins, None) for b in (1, 2, 4, 8)]
+        # "B1_grouped": gate and up in one launch (gate's token for both), then down;
+        # "B<b>_grouped": gate and up's gates for the batch in one launch, then
+        # each linear's union product, then down
+        legs = [("B1_grouped", 1, lins, [[0, 1], [2]]), ("B1", 1, lins, None)]
+        for b in (2, 4, 8):
+            legs += [(f"B{b}_grouped", b, lins, [[0, 1], [2]]), (f"B{b}", b, lins, None)]
+        return legs
     if name == "qwen_ffn_b16":
         legs = []
         for p in (0.65, 0.90):
             lins = [(5, li, dict(gate="topk", K=wl.k_from_sparsity(wl.CONFIGS[5].linears[li].n, p)))
                     for li in range(3)]
+            # gate and up share x: their 2 x 16 gates in one launch ("_grouped")
+            legs.append((f"p{int(p * 100)}_grouped", 16, lins, [[0, 1], [2]]))
             legs.append((f"p{int(p * 100)}", 16, lins, None))
         return legs
     raise ValueError(name)
@@ -494,9 +501,10 @@ def run_workload(args):
         def unit_step(u, dense=False):
             def f(i, s):
                 if len(u) > 1 and not dense:
-                    # one token: a group's linears share x (the token of its first linear)
-                    fas.sparse_linear_forward_group([rings[L][i % R].handle for L in u], Xs[u[0]][i % NT].data_ptr(),
-                                                    [Ys[L][i % R].data_ptr() for L in u], fas.SL_F32, s)
+                    # a group's linears share x (the tokens of its first linear)
+                    fas.sparse_linear_forward_group_batch([rings[L][i % R].handle for L in u],
+                                                          Xs[u[0]][i % NT].data_ptr(), B,
+                                                          [Ys[L][i % R].data_ptr() for L in u], fas.SL_F32, s)
                     return
                 for L in u:
                     h = rings[L][i % R]
@@ -559,7 +567,8 @@ def run_workload(args):
         dense_us_step = dev_s / dsteps * 1e6
         density = touched_w / total
         kernel = ("fused_group_kernel" if groups is not None else "fused_kernel") if B == 1 else \
-            "gate_kernel + union_kernel (per linear)"
+            ("gate_group_kernel + union_kernel (per linear)" if groups is not None else
+             "gate_kernel + union_kernel (per linear)")
         res = {"B": B, "tokens_per_s": B * args.steps / ev, "us_per_step": us_step,
                "wall_us_per_step": wall / args.steps * 1e6,
                "launch_us_sum": sum(unit_us), "algorithmic_bytes": tot_bytes,

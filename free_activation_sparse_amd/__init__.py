@@ -33,7 +33,7 @@ EXPORTED = [
     "sparse_linear_last_error", "sparse_linear_normal_quantile",
     "sparse_linear_forward_stages", "sparse_linear_set_plan", "sparse_linear_set_deterministic",
     "sparse_linear_set_union_plan", "sparse_linear_set_fused", "sparse_linear_sync_status",
-    "sparse_linear_forward_group", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
+    "sparse_linear_forward_group", "sparse_linear_forward_group_batch", "sparse_linear_ffn_workspace_bytes", "sparse_linear_forward_ffn",
     "sparse_linear_forward_ffn_noalloc",
     "sparse_linear_gather_ceiling", "sparse_linear_set_timeline", "ds_label_cache_update", "ds_decode_attention",
 ]
@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
     L.sparse_linear_forward_dense.restype = ctypes.c_int
     L.sparse_linear_forward_group.argtypes = [_vp, _i32, _vp, _vp, ctypes.c_int, _vp]
     L.sparse_linear_forward_group.restype = ctypes.c_int
+    L.sparse_linear_forward_group_batch.argtypes = [_vp, _i32, _vp, _i32, _vp, ctypes.c_int, _vp]
+    L.sparse_linear_forward_group_batch.restype = ctypes.c_int
     L.sparse_linear_ffn_workspace_bytes.argtypes = [_vp]
     L.sparse_linear_ffn_workspace_bytes.restype = _i64
     L.sparse_linear_forward_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.c_int, _vp, _i64, _vp]
@@ -137,6 +139,15 @@ def sparse_linear_forward_group(handles, x_ptr: int, y_ptrs, y_dtype: int, strea
     ya = (_vp * max(1, count))(*y_ptrs)
     _check(lib().sparse_linear_forward_group(ha, count, x_ptr, ya, y_dtype, stream or None),
            "sparse_linear_forward_group")
+
+
+def sparse_linear_forward_group_batch(handles, x_ptr: int, B: int, y_ptrs, y_dtype: int, stream: int = 0) -> None:
+    """B tokens ([B][n]) through len(handles) linears that share x."""
+    count = len(handles)
+    ha = (_vp * max(1, count))(*handles)
+    ya = (_vp * max(1, count))(*y_ptrs)
+    _check(lib().sparse_linear_forward_group_batch(ha, count, x_ptr, B, ya, y_dtype, stream or None),
+           "sparse_linear_forward_group_batch")
 
 
 def sparse_linear_ffn_workspace_bytes(up: int) -> int:
@@ -295,14 +306,23 @@ class SparseLinear:
 
     @staticmethod
     def forward_group(layers, x, ys=None, y_dtype=None):
-        """y_l = layers[l](x) for one token x shared by every layer (same n and
-        dtype), in one launch where possible; returns the list of y."""
+        """y_l = layers[l](x) for x shared by every layer (same n and dtype):
+        one token ([n]) in one launch where possible, or B tokens ([B][n])
+        with every layer's gates in one launch; returns the list of y ([m] or
+        [B][m])."""
         torch = layers[0]._torch
         y_dtype = torch.float32 if y_dtype is None else y_dtype
+        lead = tuple(x.shape[:-1]) if x.dim() > 1 else ()
+        B = x.shape[0] if x.dim() > 1 else 1
         if ys is None:
-            ys = [torch.empty((l.m,), dtype=y_dtype, device=l.device) for l in layers]
-        sparse_linear_forward_group([l.handle for l in layers], x.data_ptr(), [y.data_ptr() for y in ys],
-                                    SL_BF16 if ys[0].dtype == torch.bfloat16 else SL_F32, layers[0]._stream())
+            ys = [torch.empty(lead + (l.m,), dtype=y_dtype, device=l.device) for l in layers]
+        ydt = SL_BF16 if ys[0].dtype == torch.bfloat16 else SL_F32
+        if x.dim() > 1:
+            sparse_linear_forward_group_batch([l.handle for l in layers], x.data_ptr(), B,
+                                              [y.data_ptr() for y in ys], ydt, layers[0]._stream())
+        else:
+            sparse_linear_forward_group([l.handle for l in layers], x.data_ptr(), [y.data_ptr() for y in ys], ydt,
+                                        layers[0]._stream())
         return ys
 
     @staticmethod

@@ -432,53 +432,94 @@ sl_status sparse_linear_forward(sl_handle h, const void* x, int32_t B, void* y, 
   }
 }
 
-sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, const void* x, void* const* ys,
-                                      sl_dtype y_dtype, void* stream) {
-  try {
-    g_last_error.clear();
-    if (handles == nullptr || ys == nullptr || x == nullptr) return fail(SL_ERR_ARG, "NULL argument");
-    if (count < 1 || count > sl::kMaxGroupLinears)
-      return fail(SL_ERR_ARG, "count=%d outside [1, %d]", (int)count, sl::kMaxGroupLinears);
-    if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
-    for (int l = 0; l < count; ++l) {
-      const sl_linear* h = handles[l];
-      if (h == nullptr || ys[l] == nullptr) return fail(SL_ERR_ARG, "handle or y %d is NULL", l);
-      if (h->n != handles[0]->n || h->wdt != handles[0]->wdt)
-        return fail(SL_ERR_ARG, "linear %d: n or weight dtype differs from linear 0", l);
-      sl_status st = check_device(h);
-      if (st != SL_OK) return st;
-    }
-    // one handle twice would make two linears of the launch share its
-    // hand-off state and scratch
-    for (int a = 0; a < count; ++a)
-      for (int b = a + 1; b < count; ++b)
-        if (handles[a] == handles[b]) return fail(SL_ERR_ARG, "linears %d and %d are the same handle", a, b);
-    for (int l = 0; l < count; ++l) {
-      sl_status st = take_async_error(handles[l]);
-      if (st != SL_OK) return st;
-    }
-    bool grouped = count > 1 && y_dtype == SL_F32;
-    for (int l = 0; l < count && grouped; ++l) {
-      const sl_linear* h = handles[l];
-      grouped = h->fused && !h->deterministic && h->gate == handles[0]->gate && sl::fused_supported(h, x);
-    }
+static sl_status group_impl(const sl_handle* handles, int32_t count, const void* x, int32_t B, void* const* ys,
+                            sl_dtype y_dtype, void* stream) {
+  g_last_error.clear();
+  if (handles == nullptr || ys == nullptr || x == nullptr) return fail(SL_ERR_ARG, "NULL argument");
+  if (count < 1 || count > sl::kMaxGroupLinears)
+    return fail(SL_ERR_ARG, "count=%d outside [1, %d]", (int)count, sl::kMaxGroupLinears);
+  if (y_dtype != SL_F32 && y_dtype != SL_BF16) return fail(SL_ERR_ARG, "bad y_dtype %d", (int)y_dtype);
+  if (B < 1) return fail(SL_ERR_ARG, "B=%d must be >= 1", (int)B);
+  for (int l = 0; l < count; ++l) {
+    const sl_linear* h = handles[l];
+    if (h == nullptr || ys[l] == nullptr) return fail(SL_ERR_ARG, "handle or y %d is NULL", l);
+    if (h->n != handles[0]->n || h->wdt != handles[0]->wdt)
+      return fail(SL_ERR_ARG, "linear %d: n or weight dtype differs from linear 0", l);
+    if (B > h->max_batch) return fail(SL_ERR_ARG, "linear %d: B=%d above its max_batch=%d", l, (int)B, h->max_batch);
+    sl_status st = check_device(h);
+    if (st != SL_OK) return st;
+  }
+  // one handle twice would make two linears of the launch share its
+  // hand-off state and scratch
+  for (int a = 0; a < count; ++a)
+    for (int b = a + 1; b < count; ++b)
+      if (handles[a] == handles[b]) return fail(SL_ERR_ARG, "linears %d and %d are the same handle", a, b);
+  for (int l = 0; l < count; ++l) {
+    sl_status st = take_async_error(handles[l]);
+    if (st != SL_OK) return st;
+  }
+  const sl_linear* hs[sl::kMaxGroupLinears];
+  for (int l = 0; l < count; ++l) hs[l] = handles[l];
+  hipStream_t s = (hipStream_t)stream;
+  if (B > 1) {
+    // the linears' gates for the B tokens in one launch, then each linear's
+    // matrix-core pass over the union of its B kept sets
+    bool grouped = count > 1;
+    for (int l = 0; l < count && grouped; ++l)
+      grouped = hs[l]->wdt == SL_BF16 && hs[l]->gate == hs[0]->gate && hs[l]->gate != SL_GATE_FIXED;
     if (!grouped) {
       for (int l = 0; l < count; ++l) {
-        sl_status st = forward_impl(handles[l], x, 1, ys[l], y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
+        sl_status st = forward_impl(handles[l], x, B, ys[l], y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
         if (st != SL_OK) return st;
       }
       return SL_OK;
     }
-    const sl_linear* hs[sl::kMaxGroupLinears];
-    float* yf[sl::kMaxGroupLinears];
+    float* zy[sl::kMaxGroupLinears];
     for (int l = 0; l < count; ++l) {
-      hs[l] = handles[l];
-      yf[l] = (float*)ys[l];
+      const sl::UnionPlan up = make_union_plan(hs[l], y_dtype);
+      zy[l] = (up.atomic && up.splits > 1) ? (float*)ys[l] : nullptr;
     }
-    SL_HIP(sl::launch_fused_group(hs, count, x, yf, (hipStream_t)stream));
+    SL_HIP(sl::launch_gate_group(hs, count, x, B, zy, s));
+    for (int l = 0; l < count; ++l) {
+      sl::UnionPlan up = make_union_plan(hs[l], y_dtype);
+      up.spec = union_spec(hs[l], B, false);
+      SL_HIP(sl::launch_union_product(hs[l], up, x, B, false, ys[l], y_dtype, s));
+    }
     return SL_OK;
+  }
+  bool grouped = count > 1 && y_dtype == SL_F32;
+  for (int l = 0; l < count && grouped; ++l) {
+    const sl_linear* h = handles[l];
+    grouped = h->fused && !h->deterministic && h->gate == handles[0]->gate && sl::fused_supported(h, x);
+  }
+  if (!grouped) {
+    for (int l = 0; l < count; ++l) {
+      sl_status st = forward_impl(handles[l], x, 1, ys[l], y_dtype, nullptr, nullptr, nullptr, stream, false, 3);
+      if (st != SL_OK) return st;
+    }
+    return SL_OK;
+  }
+  float* yf[sl::kMaxGroupLinears];
+  for (int l = 0; l < count; ++l) yf[l] = (float*)ys[l];
+  SL_HIP(sl::launch_fused_group(hs, count, x, yf, s));
+  return SL_OK;
+}
+
+sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, const void* x, void* const* ys,
+                                      sl_dtype y_dtype, void* stream) {
+  try {
+    return group_impl(handles, count, x, 1, ys, y_dtype, stream);
   } catch (...) {
     return fail(SL_ERR_OOM, "unexpected host exception in forward_group");
+  }
+}
+
+sl_status sparse_linear_forward_group_batch(const sl_handle* handles, int32_t count, const void* x, int32_t B,
+                                            void* const* ys, sl_dtype y_dtype, void* stream) {
+  try {
+    return group_impl(handles, count, x, B, ys, y_dtype, stream);
+  } catch (...) {
+    return fail(SL_ERR_OOM, "unexpected host exception in forward_group_batch");
   }
 }
 

@@ -128,6 +128,11 @@ hipError_t launch_silu_mul(const float* g, const float* u, uint16_t* h, int64_t 
 // Grouped fused forward (one token) of count <= 8 linears that share x: all
 // fused_supported, the same n and gate mode, fp32 y, atomic reduction.
 constexpr int kMaxGroupLinears = 8;
+// The gates of `count` bf16 linears that share x ([B][n]), top-K or
+// statistical (the same mode), in one launch; zero_y[l] (or NULL) is cleared
+// for linear l's atomic union product.
+hipError_t launch_gate_group(const sl_linear* const* hs, int count, const void* x, int B, float* const* zero_y,
+                             hipStream_t s);
 hipError_t launch_fused_group(const sl_linear* const* hs, int count, const void* x, float* const* ys,
                               hipStream_t s);
 // Fused gate + product for one token (bf16 weights, any gate, n % 4 == 0 and

@@ -160,6 +160,28 @@ sl_status sparse_linear_forward_group(const sl_handle* handles, int32_t count, c
                                       sl_dtype y_dtype, void* stream);
 
 /*
+ * sparse_linear_forward_group_batch -- sparse_linear_forward_group for a
+ * batch of B tokens (WINA article, section 一: each token keeps its own
+ * inputs, per linear).
+ *
+ *   x          device [B][n], the weights' dtype.
+ *   ys         host array of `count` device pointers, ys[l] of [B][m_l] y_dtype.
+ *   B          1 <= B <= every handle's max_batch.
+ *
+ * B == 1 is sparse_linear_forward_group. For B > 1 with bf16 weights and a
+ * top-K or statistical gate shared by all linears, one launch runs every
+ * linear's gate for every token (count * B workgroups), then each linear's
+ * matrix-core pass over the union of its B kept sets follows, as in
+ * sparse_linear_forward; otherwise the linears run one after another.
+ * y_l equals sparse_linear_forward(handles[l], x, B, ys[l], ...) up to the
+ * split reduction's summation order. No mask, count or threshold outputs.
+ * Errors: those of sparse_linear_forward_group, and B outside
+ * [1, max_batch] of any handle (SL_ERR_ARG); nothing is launched then.
+ */
+sl_status sparse_linear_forward_group_batch(const sl_handle* handles, int32_t count, const void* x, int32_t B,
+                                            void* const* ys, sl_dtype y_dtype, void* stream);
+
+/*
  * Sparse FFN chain for one token (Spark Transformer article, section 2.1: the
  * FFN scores, selects and computes only the selected part; WINA article,
  * section 一: each projection keeps its inputs by |x_j c_j|):

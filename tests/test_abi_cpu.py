@@ -131,6 +131,19 @@ def test_forward_group_rejects_bad_arguments(slib):
     assert "handle" in slib.sparse_linear_last_error() or "dtype" in slib.sparse_linear_last_error()
 
 
+def test_forward_group_batch_rejects_bad_arguments(slib):
+    L = slib.lib()
+    hs = (ctypes.c_void_p * 2)(None, None)
+    ys = (ctypes.c_void_p * 2)(1, 1)
+    assert L.sparse_linear_forward_group_batch(None, 1, 1, 2, ys, 0, None) == 1  # NULL handle array
+    assert L.sparse_linear_forward_group_batch(hs, 1, 1, 2, None, 0, None) == 1  # NULL y array
+    assert L.sparse_linear_forward_group_batch(hs, 1, None, 2, ys, 0, None) == 1  # NULL x
+    assert L.sparse_linear_forward_group_batch(hs, 9, 1, 2, ys, 0, None) == 1    # count > 8
+    assert L.sparse_linear_forward_group_batch(hs, 1, 1, 0, ys, 0, None) == 1    # B < 1
+    assert L.sparse_linear_forward_group_batch(hs, 2, 1, 2, ys, 0, None) == 1    # NULL handles
+    assert "B=" in slib.sparse_linear_last_error() or "handle" in slib.sparse_linear_last_error()
+
+
 def test_strerror(slib):
     assert slib.sparse_linear_strerror(0) == "success"
     assert slib.sparse_linear_strerror(2) == "unsupported shape or alignment"

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from parity_util import REL_L2_TOL, gate_kwargs, rel_l2, to_dev
+from parity_util import REL_L2_TOL, gate_kwargs, rel_l2, tile_rows, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -174,4 +174,72 @@ def test_group_and_ffn_reject_duplicate_handles(fas):
     for l in ls:
         l.sync_status()
     for l in ls:
+        l.close()
+
+
+def _layer_b(fas, W, c, mode, B, **g):
+    return fas.SparseLinear(to_dev(W, torch), c=to_dev(c, torch), max_batch=B, **gate_kwargs(mode, **g))
+
+
+@pytest.mark.parametrize("cfg,mode,B,g", [(5, "topk", 16, 0.65), (5, "topk", 3, 0.9), (4, "stat", 4, 0.10),
+                                          (4, "stat", 2, 0.10)])
+def test_group_batch_gate_up(fas, cfg, mode, B, g):
+    """A batch through the gate and up projections of the Qwen-2.5-7B and
+    Phi-4 FFNs (sparse_linear_forward_group_batch: both linears' gates for
+    every token in one launch, then each linear's union product): every
+    token's y of every linear matches the oracle on that token and linear
+    (rows of every 256-row tile), and the linear's own batched forward up to
+    summation order; twice, the second time with the first call's
+    thresholds as the gates' prior."""
+    lins = wl.CONFIGS[cfg].linears
+    idx = [li for li, l in enumerate(lins) if l.name in ("gate", "up")]
+    Ws = [wl.weight(cfg, li) for li in idx]
+    cs = [oracle.column_norms(W) for W in Ws]
+    if mode == "topk":
+        gs = [dict(K=wl.k_from_sparsity(lins[li].n, g)) for li in idx]
+    else:
+        gs = [dict(s_keep=g) for _ in idx]
+    layers = [_layer_b(fas, W, c, mode, B, **gg) for W, c, gg in zip(Ws, cs, gs)]
+    m = Ws[0].shape[0]
+    rows = tile_rows(m, 5)
+    for call in range(2):
+        X = wl.tokens(cfg, idx[0], 200 + 16 * call, B)
+        xd = to_dev(X, torch)
+        print(f"[group batch cfg {cfg} {mode} B={B}] call {call}", flush=True)
+        ys = fas.SparseLinear.forward_group(layers, xd)
+        for l in layers:
+            l.sync_status()
+        for i, (layer, W, c, gg) in enumerate(zip(layers, Ws, cs, gs)):
+            single = layer.forward(xd)["y"]
+            layer.sync_status()
+            got = ys[i].cpu().numpy()
+            assert rel_l2(got, single.cpu().numpy()) <= 1e-5, f"linear {i} call {call}: vs batched forward"
+            for b in range(B):
+                ref = oracle.forward(W, c, X[b], mode, rows=rows, **gg)
+                err = rel_l2(got[b][rows], ref["y"])
+                assert err <= REL_L2_TOL, f"linear {i} call {call} token {b}: rel L2 {err:.3e}"
+    for l in layers:
+        l.close()
+
+
+def test_group_batch_falls_back(fas):
+    """Mixed gate modes in one batch call run the linears one after another
+    (same results as their own forwards); B above a handle's max_batch is
+    rejected."""
+    m, n, B = 512, 2048, 4
+    W1, W2 = wl.random_matrix(150, m, n, "bf16"), wl.random_matrix(151, m, n, "bf16")
+    c1, c2 = oracle.column_norms(W1), oracle.column_norms(W2)
+    a = _layer_b(fas, W1, c1, "topk", B, K=700)
+    b = _layer_b(fas, W2, c2, "stat", B, s_keep=0.2)
+    X = wl.random_tokens(152, B, n, "bf16", "laplace")
+    xd = to_dev(X, torch)
+    ys = fas.SparseLinear.forward_group([a, b], xd)
+    for layer, y in ((a, ys[0]), (b, ys[1])):
+        single = layer.forward(xd)["y"]
+        layer.sync_status()
+        assert rel_l2(y.cpu().numpy(), single.cpu().numpy()) <= 1e-5
+    small = _layer_b(fas, W2, c2, "topk", 2, K=100)
+    with pytest.raises(fas.SparseLinearError):
+        fas.SparseLinear.forward_group([a, small], xd)
+    for l in (a, b, small):
         l.close()
