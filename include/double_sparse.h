@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define DS_MAX_SEQ 32768  /* cached tokens per sequence (scores live in registers) */
 #define DS_MAX_K 8192     /* kept tokens when k < max_seq (the kept list lives in LDS) */
 

@@ -61,7 +61,7 @@ typedef enum {
   SL_GATE_FIXED = 2  /* calibrated per-layer threshold: keep score > tau    */
 } sl_gate;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define SL_MAX_N 32768     /* inputs per token (the gate keeps them in LDS) */
 #define SL_MAX_BATCH 16    /* tokens per forward                              */
 
